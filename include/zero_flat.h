@@ -1,0 +1,278 @@
+/*
+ * zero_flat.h -- C ABI for one data-parallel rank's share of a ZeRO
+ * mixed-precision Adam step on MI355X (gfx950).
+ *
+ * The interface follows the pages' statement of the problem (ZeRO reading
+ * notes 026, §三 pseudocode): partition the parameter indices and assign an
+ * owner to each; decide per stage what is sharded; bring each shard's gradient
+ * to its owner; let each owner update its shard with its local optimizer
+ * state; gather the updated parameters.
+ *
+ * Conventions for every function
+ * ------------------------------
+ * - Return value: ZERO_OK (0) or a negative ZERO_E* code; zero_last_error()
+ *   then holds a message for the calling thread.  Every argument is checked
+ *   BEFORE anything is enqueued: on error nothing has been launched and no
+ *   output has been touched (the pages' validate-then-act rule: L18 notes §5.1
+ *   and §5.4; fail explicitly, never partially: 026 notes §五).
+ * - Device buffers are owned by the caller (allocated with any allocator,
+ *   e.g. PyTorch).  The library allocates no device memory; kernels that need
+ *   scratch use the caller's workspace (zero_workspace_bytes).
+ * - Device work is enqueued asynchronously on `stream` (a hipStream_t passed
+ *   as void*; NULL = the null stream) on the current HIP device.  Results are
+ *   valid once the stream reaches that point.  Calls are re-entrant; calls
+ *   that share a workspace or flag must be ordered on one stream.
+ * - 16-bit data: ZERO_F16 (IEEE binary16) or ZERO_BF16.  Optimizer state is
+ *   always fp32.  Element counts are int64; n = 0 is a no-op (where a device
+ *   output is defined for n = 0, e.g. the norm, it is still written).
+ * - Alignment: 16-bit pointers 2-byte aligned, fp32 pointers 4-byte aligned.
+ *   Any offset works; 16-byte-aligned buffers take the vector path.
+ * - Inputs may not overlap outputs (ZERO_EALIAS).
+ * - A non-finite gradient is not an error: it is reported through the
+ *   caller's int32 device flag and the Adam kernel then skips the step.
+ */
+#ifndef ZERO_FLAT_H
+#define ZERO_FLAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_OK 0
+#define ZERO_EINVAL (-1)  /* bad pointer, size, rank count, stage or dtype */
+#define ZERO_EALIAS (-2)  /* an output overlaps an input or another output */
+#define ZERO_EHIP (-3)    /* the HIP runtime refused a launch or copy */
+#define ZERO_ENOMEM (-4)  /* host allocation for a plan failed */
+
+#define ZERO_F16 1
+#define ZERO_BF16 2
+
+#define ZERO_MAX_RANKS 1024
+
+/* Bits of the int32 step flag (device memory, OR-ed by the kernels). */
+#define ZERO_FLAG_NONFINITE_GRAD 1 /* an input or reduced gradient is inf/NaN */
+#define ZERO_FLAG_NONFINITE_NORM 2 /* the sum of squares is not finite */
+
+/* ---------------------------------------------------------------------- */
+/* a0: partition (host only, integer arithmetic)                           */
+/* ---------------------------------------------------------------------- */
+
+/* Opaque plan; created and destroyed on the host. */
+typedef struct zero_plan zero_plan;
+
+/* A piece of a named tensor that a rank owns. */
+typedef struct {
+    int64_t tensor;     /* index into the tensor list */
+    int64_t tensor_off; /* first element of the piece inside the tensor */
+    int64_t shard_off;  /* where the piece starts in the rank's shard */
+    int64_t len;        /* elements */
+} zero_segment;
+
+/*
+ * zero_plan_create -- flat-bucket partition of `n_units` units over `nd` ranks.
+ *
+ * Adam is elementwise, so rank r only needs the state of its own piece of
+ * the flat parameter vector (L18 notes §2.1); the parameters are flattened
+ * into one vector and cut into nd equal pieces, a tensor may straddle two
+ * ranks (L18 notes §3.2, exercise 6).  ZeRO-3 flattens and splits per module
+ * (Illustrated ZeRO §8.4).
+ *
+ * stage 0: plain data parallelism, one owner holds everything.
+ * stage 1, 2: the units are concatenated into ONE flat unit.
+ * stage 3: each unit (e.g. a layer) is partitioned separately.
+ * Each unit of U elements gets slice s = roundup(ceil(U / owners), align);
+ * rank r owns unit-local padded positions [r*s, (r+1)*s); positions >= U
+ * are padding.  Units are laid out back to back in the padded full buffer,
+ * and their slices back to back in every rank's shard.
+ *
+ * unit_numels: host array of n_units sizes >= 0 (sum > 0); 1 <= nd <= 1024;
+ * align_elems >= 1.  On success *out receives a plan the caller frees with
+ * zero_plan_destroy.  Errors: ZERO_EINVAL, ZERO_ENOMEM.
+ */
+int zero_plan_create(const int64_t* unit_numels, int n_units, int nd, int stage,
+                     int64_t align_elems, zero_plan** out);
+void zero_plan_destroy(zero_plan* plan);
+
+/* Number of units after merging (1 for stages 0-2) and number of owners. */
+int zero_plan_info(const zero_plan* plan, int* n_units, int* owners, int* nd, int* stage);
+
+/* Per-rank shard length (padded, the same for every rank) and the real
+ * (non-padding) elements rank `rank` owns. */
+int zero_plan_rank(const zero_plan* plan, int rank, int64_t* shard_numel, int64_t* real_numel);
+
+/* Unit `unit`: real size, slice per owner, base in the padded full buffer,
+ * base inside every shard. */
+int zero_plan_unit(const zero_plan* plan, int unit, int64_t* numel, int64_t* slice_numel,
+                   int64_t* full_base, int64_t* shard_base);
+
+/* Padded length of the full gather buffer. */
+int zero_plan_full_numel(const zero_plan* plan, int64_t* padded);
+
+/*
+ * zero_plan_segments -- the pieces of named tensors rank `rank` owns, in shard
+ * order.  Tensors (host array of n_tensors sizes) fill the plan's units back to
+ * back; for stage 3 a tensor may not cross a unit.  Writes at most `cap`
+ * segments to `out` and the total number to *count (call with cap = 0 to
+ * size the array).  Errors: ZERO_EINVAL (sizes do not fill the units).
+ */
+int zero_plan_segments(const zero_plan* plan, const int64_t* tensor_numels, int n_tensors,
+                       int rank, zero_segment* out, int cap, int* count);
+
+/* ---------------------------------------------------------------------- */
+/* Accounting (host only)                                                  */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Per-rank model-state bytes for psi parameters: stage 0 (4+K)psi, stage 1
+ * 4psi + K psi/nd, stage 2 2psi + (2+K)psi/nd, stage 3 (4+K)psi/nd, with K
+ * optimizer bytes per parameter (12 for fp32 master + m + v).  L18 notes
+ * §1.2, §2.1; L3.2 §2.3.
+ */
+int zero_model_state_bytes(double psi, int nd, int stage, int k_bytes, double* out);
+
+/* Elements one rank sends per step: 2psi (stages 0-2) or 3psi (stage 3), each
+ * times (nd-1)/nd.  L18 notes §3.1; ZeRO paper notes 0x07. */
+int zero_comm_volume(double psi, int nd, int stage, double* elems_sent);
+
+/* ---------------------------------------------------------------------- */
+/* Workspace                                                               */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Bytes of device workspace for `n_sets` partial-sum sets over shards of n
+ * elements.  The workspace holds, per set, the fp64 sums of squares of one
+ * reduce (or partials) launch, plus a table of up to ZERO_MAX_RANKS device
+ * pointers.  The caller allocates it (any alignment >= 8) and passes it to
+ * zero_reduce_shard / zero_grad_norm / zero_gather_params; its contents need no
+ * initialisation.  Returns -1 on bad arguments.
+ */
+int64_t zero_workspace_bytes(int64_t n, int n_sets);
+
+/* ---------------------------------------------------------------------- */
+/* a1: local half of the reduce-scatter                                    */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * zero_reduce_shard -- the owner's averaged gradient slice.
+ *
+ * The owner receives the AVERAGE gradient of its slice (L18 notes §2.2 step 3;
+ * ZeRO paper notes 0x05 §5.2), summed in a fixed rank order (L18 notes §2.5):
+ *   acc = f32(c_0[i]); acc += f32(c_r[i]) for r = 1..nd-1   (fp32, no FMA)
+ *   reduced_out[i] = round_to_nearest_even_16(acc / nd)
+ * The loss scale stays in the stored value.  Fused into the same pass:
+ *   - per-block fp64 sums of (f32(reduced_out[i]) * inv_loss_scale)^2 into
+ *     workspace set `set` (consumed by zero_grad_norm);
+ *   - *flag |= ZERO_FLAG_NONFINITE_GRAD if any c_r[i] or reduced_out[i] is
+ *     inf/NaN.  The flag is OR-ed, never cleared: zero it once per step.
+ *
+ * contribs: HOST array of nd device pointers, each to n 16-bit values of
+ *   `dtype` (rank 0 first).  1 <= nd <= 1024.
+ * reduced_out: device, n values of `dtype`; may not overlap any contribution.
+ * inv_loss_scale: a positive power of two (1 when no loss scaling).
+ * workspace / workspace_bytes: >= zero_workspace_bytes(n, set + 1).
+ * flag: device int32.
+ */
+int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
+                      float inv_loss_scale, void* reduced_out, void* workspace,
+                      int64_t workspace_bytes, int set, int32_t* flag, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* a2: global gradient norm and clip coefficient                           */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * zero_grad_norm -- L2 norm over the flat gradient and the clip multiplier
+ * (L18 notes §1.4; L3.2 §4.2 gradient_clipping).
+ *
+ * If `grad` is not NULL, first a partials pass over grad[0..n) (16-bit,
+ * `dtype`) writes set 0 of the workspace (as zero_reduce_shard would) and ORs
+ * ZERO_FLAG_NONFINITE_GRAD into *flag for inf/NaN -- this is the path for an
+ * already-reduced gradient.  Then one block sums, in fp64 and in a fixed order,
+ * sets 0..n_sets-1 of the workspace (set-major, the order the ranks were
+ * reduced in) followed by extra_sumsq[0..n_extra) (device fp64, e.g. other
+ * ranks' sums; may be NULL when n_extra = 0):
+ *   norm = sqrt(sumsq)
+ *   coef = (float)min(1, max_norm / (norm + 1e-6))   (fp64; max_norm <= 0: 1)
+ * If the sum is not finite, *flag |= ZERO_FLAG_NONFINITE_NORM.  norm_out
+ * (device fp64) and coef_out (device fp32) are always written.  The result is
+ * bitwise repeatable: the summation tree depends only on n and n_sets.
+ *
+ * n is the per-set shard length used by the producing launches; 1 <= n_sets.
+ */
+int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
+                   void* workspace, int64_t workspace_bytes, int n_sets,
+                   const double* extra_sumsq, int n_extra, float max_norm, int32_t* flag,
+                   double* norm_out, float* coef_out, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* a3: fused Adam(W) on the owned fp32 state, writing the 16-bit parameter */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;   /* decoupled (AdamW); 0 = plain Adam */
+    float inv_loss_scale; /* positive power of two */
+    int64_t step;         /* t >= 1; bias corrections f32(1 - beta^t) from fp64 */
+} zero_adam_hparams;
+
+/*
+ * zero_adam_step -- the owner updates its fp32 variance, momentum and master,
+ * then copies the master to the 16-bit parameter (L18 notes §2.2 step 4;
+ * Adam is elementwise, §2.1).  Per element, in fp32:
+ *   g  = f32(grad[i]) * inv_loss_scale * (*coef_dev)
+ *   m  = beta1 m + (1 - beta1) g
+ *   v  = beta2 v + (1 - beta2) g^2
+ *   p  = p - lr * ( (m / bc1) / (sqrt(v / bc2) + eps) + weight_decay * p )
+ *   param_out[i] = round_to_nearest_even_16(p)
+ * master, m and v are each read once and written once.  If *flag != 0 the
+ * kernel writes nothing (the step is skipped).
+ *
+ * master, m, v: device fp32, n each, distinct.  grad: device 16-bit
+ * (`grad_dtype`), n.  coef_dev: device fp32 (from zero_grad_norm).  flag:
+ * device int32.  param_out: device 16-bit (`param_dtype`), n -- typically the
+ * full gather buffer plus this rank's offset, so the cast lands in place.
+ */
+int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad_dtype,
+                   int64_t n, const zero_adam_hparams* hp, const float* coef_dev,
+                   const int32_t* flag, void* param_out, int param_dtype, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* a4: gather of 16-bit shards into the full parameter buffer              */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * zero_gather_params -- all-gather of the updated 16-bit slices (L18 notes
+ * §2.2 step 5), unit by unit: ZeRO-3 gathers one module's parameters into a
+ * contiguous buffer (Illustrated ZeRO §8.4).  A pure copy, for every unit u in
+ * [unit_begin, unit_end) and owner r:
+ *   full[full_base_u + r*s_u + j] = shards[r][shard_base_u + j],  j < s_u
+ * shards: HOST array of `owners` device pointers (plan's owner count), each
+ * to shard_numel 16-bit values.  full: device, plan's padded full length.
+ * workspace: >= zero_workspace_bytes(0, 0) bytes (holds the pointer table
+ * when there are more than 64 owners; may be NULL otherwise).
+ */
+int zero_gather_params(const zero_plan* plan, const void* const* shards, int unit_begin,
+                       int unit_end, int dtype, void* full, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Misc                                                                    */
+/* ---------------------------------------------------------------------- */
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* zero_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int zero_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_FLAT_H */

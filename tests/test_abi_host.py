@@ -1,0 +1,192 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, its partitioner and accounting agree with the oracle exactly, and
+invalid arguments are rejected before anything is launched (no GPU needed:
+none of these calls reaches the HIP runtime)."""
+
+import os
+import random
+import re
+
+import pytest
+
+from oracle import accounting, partition
+from zero_sharded_mixed_flat_amd import abi, workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "zero_flat.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_what_the_binding_knows():
+    assert _declared() == sorted(abi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in _declared():
+        assert hasattr(abi.lib, name), name
+
+
+def test_version():
+    assert abi.zero_version() == 10000
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_partition_matches_oracle(seed):
+    rng = random.Random(1000 + seed)
+    units = [rng.choice([1, 7, 8, 9, rng.randint(1, 10 ** rng.randint(1, 9))])
+             for _ in range(rng.randint(1, 8))]
+    nd = rng.choice([1, 2, 3, 4, 5, 8, 16, 64, 100, 1024])
+    stage = rng.choice([0, 1, 2, 3])
+    align = rng.choice([1, 2, 8, 64])
+    ours = abi.Plan(units, nd, stage, align)
+    ref = partition.make_plan(units, nd, stage, align)
+    info = ours.info()
+    assert info["n_units"] == len(ref.units) and info["owners"] == ref.owners
+    assert ours.full_numel() == ref.full_numel
+    for i, u in enumerate(ref.units):
+        assert ours.unit(i) == (u.numel, u.slice_numel, u.full_base, u.shard_base)
+    for r in sorted({0, nd - 1, nd // 2, rng.randrange(nd)}):
+        assert ours.rank(r) == (ref.shard_numel, ref.real_numel(r))
+    # Tensor segments: split each unit into a few tensors.
+    tensors = []
+    for u in (units if stage == 3 else [sum(units)]):
+        cuts = sorted(rng.sample(range(1, u), min(3, u - 1))) if u > 1 else []
+        tensors += [b - a for a, b in zip([0] + cuts, cuts + [u])]
+    for r in sorted({0, nd - 1, rng.randrange(nd)}):
+        assert ours.segments(tensors, r) == partition.segments(ref, tensors, r)
+
+
+def test_workload_layouts_match_oracle():
+    for w in workloads.WORKLOADS.values():
+        ours = abi.Plan(w.units, w.nd, w.stage, w.align)
+        ref = partition.make_plan(w.units, w.nd, w.stage, w.align)
+        assert ours.rank(w.rank) == (ref.shard_numel, ref.real_numel(w.rank)), w.name
+        assert ours.full_numel() == ref.full_numel, w.name
+        if w.tensors:
+            assert ours.segments(w.tensors, w.rank) == partition.segments(ref, w.tensors, w.rank)
+
+
+@pytest.mark.parametrize("stage", [0, 1, 2, 3])
+@pytest.mark.parametrize("nd", [1, 4, 16, 64])
+def test_accounting_matches_oracle(stage, nd):
+    for psi in (1.0, 7.5e9, 175e9):
+        for k in (12, 16):
+            assert abi.zero_model_state_bytes(psi, nd, stage, k) == accounting.model_state_bytes(psi, nd, stage, k)
+        assert abi.zero_comm_volume(psi, nd, stage) == pytest.approx(accounting.comm_volume(psi, nd, stage),
+                                                                     rel=1e-15)
+
+
+def test_plan_rejects_bad_arguments():
+    for args in (([10], 0, 1, 8), ([10], 1025, 1, 8), ([10], 2, 4, 8), ([10], 2, 1, 0), ([0, 0], 2, 1, 8),
+                 ([-1], 2, 1, 8)):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.Plan(*args)
+        assert e.value.code == abi.ZERO_EINVAL
+    p = abi.Plan([10, 20], 2, 3, 8)
+    with pytest.raises(abi.ZeroError):
+        p.segments([10, 21], 0)          # sizes do not add up
+    with pytest.raises(abi.ZeroError):
+        p.segments([15, 15], 0)          # a tensor crosses a unit
+    with pytest.raises(abi.ZeroError):
+        p.rank(2)
+
+
+def test_workspace_bytes():
+    assert abi.zero_workspace_bytes(0, 0) == 8192
+    assert abi.zero_workspace_bytes(8 * 256, 1) == 8192 + 8
+    assert abi.zero_workspace_bytes(10 ** 10, 2) == 8192 + 2 * 2048 * 8
+    with pytest.raises(abi.ZeroError):
+        abi.zero_workspace_bytes(-1, 1)
+
+
+# Fake, never-dereferenced device addresses: each call below must fail in
+# validation, before the HIP runtime is touched.
+A, B, W, F = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _reduce(**kw):
+    args = dict(contribs=[A, A + 4096], n=1024, dtype=abi.ZERO_F16, inv_loss_scale=1.0, reduced_out=B,
+                workspace=W, set_index=0, flag=F, stream=0,
+                workspace_bytes=abi.zero_workspace_bytes(1024, 1))
+    args.update(kw)
+    return abi.zero_reduce_shard(**args)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(contribs=[]), abi.ZERO_EINVAL),
+    (dict(n=-1), abi.ZERO_EINVAL),
+    (dict(dtype=3), abi.ZERO_EINVAL),
+    (dict(inv_loss_scale=0.3), abi.ZERO_EINVAL),
+    (dict(inv_loss_scale=0.0), abi.ZERO_EINVAL),
+    (dict(workspace_bytes=100), abi.ZERO_EINVAL),
+    (dict(set_index=1), abi.ZERO_EINVAL),
+    (dict(flag=0), abi.ZERO_EINVAL),
+    (dict(reduced_out=B + 1), abi.ZERO_EINVAL),
+    (dict(contribs=[A, 0]), abi.ZERO_EINVAL),
+    (dict(reduced_out=A + 4096 + 2046), abi.ZERO_EALIAS),
+    (dict(workspace=A + 64), abi.ZERO_EALIAS),
+])
+def test_reduce_rejects(bad, code):
+    with pytest.raises(abi.ZeroError) as e:
+        _reduce(**bad)
+    assert e.value.code == code
+
+
+def _adam(**kw):
+    args = dict(master=A, m=A + 8192, v=A + 16384, grad=B, grad_dtype="bf16", n=1024,
+                hp=abi.adam_hparams(3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 1), coef=F, flag=F + 4,
+                param_out=B + 8192, param_dtype="bf16", stream=0)
+    args.update(kw)
+    return abi.zero_adam_step(**args)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(n=-5), abi.ZERO_EINVAL),
+    (dict(grad_dtype=0), abi.ZERO_EINVAL),
+    (dict(hp=abi.adam_hparams(3e-4, 1.0, 0.95, 1e-8, 0.1, 1.0, 1)), abi.ZERO_EINVAL),
+    (dict(hp=abi.adam_hparams(3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 0)), abi.ZERO_EINVAL),
+    (dict(hp=abi.adam_hparams(float("nan"), 0.9, 0.95, 1e-8, 0.1, 1.0, 1)), abi.ZERO_EINVAL),
+    (dict(hp=abi.adam_hparams(3e-4, 0.9, 0.95, 1e-8, 0.1, 3.0, 1)), abi.ZERO_EINVAL),
+    (dict(master=A + 2), abi.ZERO_EINVAL),
+    (dict(coef=0), abi.ZERO_EINVAL),
+    (dict(m=A + 4000), abi.ZERO_EALIAS),
+    (dict(param_out=B + 100), abi.ZERO_EALIAS),
+    (dict(param_out=A + 20000), abi.ZERO_EALIAS),
+])
+def test_adam_rejects(bad, code):
+    with pytest.raises(abi.ZeroError) as e:
+        _adam(**bad)
+    assert e.value.code == code
+
+
+def test_adam_zero_length_is_a_no_op():
+    _adam(n=0, master=None, m=None, v=None, grad=None, param_out=None)
+
+
+def test_grad_norm_rejects():
+    base = dict(grad=None, n=100, dtype=1, inv_loss_scale=1.0, workspace=W, n_sets=1, extra_sumsq=None,
+                n_extra=0, max_norm=1.0, flag=F, norm_out=F + 8, coef_out=F + 16, stream=0,
+                workspace_bytes=abi.zero_workspace_bytes(100, 1))
+    for bad in (dict(n_sets=0), dict(n_extra=2), dict(max_norm=float("inf")), dict(norm_out=F + 4),
+                dict(workspace_bytes=8), dict(grad=B, dtype=7), dict(grad=W + 8)):
+        args = dict(base, **bad)
+        with pytest.raises(abi.ZeroError):
+            abi.zero_grad_norm(**args)
+
+
+def test_gather_rejects():
+    plan = abi.Plan([1000, 1000], 4, 3, 8)
+    base = dict(plan=plan, shards=[A + i * 4096 for i in range(4)], unit_begin=0, unit_end=2, dtype=1,
+                full=B, workspace=None, stream=0)
+    for bad, code in ((dict(unit_end=3), abi.ZERO_EINVAL), (dict(unit_begin=2, unit_end=1), abi.ZERO_EINVAL),
+                      (dict(dtype=9), abi.ZERO_EINVAL), (dict(full=A + 100), abi.ZERO_EALIAS),
+                      (dict(shards=[A, 0, A, A]), abi.ZERO_EINVAL)):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_gather_params(**dict(base, **bad))
+        assert e.value.code == code
+    abi.zero_gather_params(**dict(base, unit_begin=1, unit_end=1))   # empty range: no-op

@@ -1,0 +1,293 @@
+"""ctypes binding for ``include/zero_flat.h``: same function names, argument
+marshalling only.
+
+Buffers may be given as torch tensors (their ``data_ptr()`` is passed) or as
+integer device addresses.  ``stream`` defaults to torch's current HIP stream.
+Every function raises ``ZeroError`` on a non-zero status.  There is no fallback:
+if the shared library is missing, importing this module fails.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libzero_flat.so")
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EALIAS = -2
+ZERO_EHIP = -3
+ZERO_ENOMEM = -4
+ZERO_F16 = 1
+ZERO_BF16 = 2
+ZERO_MAX_RANKS = 1024
+ZERO_FLAG_NONFINITE_GRAD = 1
+ZERO_FLAG_NONFINITE_NORM = 2
+
+# Every symbol include/zero_flat.h declares.
+EXPORTED = (
+    "zero_plan_create", "zero_plan_destroy", "zero_plan_info", "zero_plan_rank", "zero_plan_unit",
+    "zero_plan_full_numel", "zero_plan_segments", "zero_model_state_bytes", "zero_comm_volume",
+    "zero_workspace_bytes", "zero_reduce_shard", "zero_grad_norm", "zero_adam_step",
+    "zero_gather_params", "zero_last_error", "zero_version",
+)
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class zero_segment(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int64), ("tensor_off", ctypes.c_int64),
+                ("shard_off", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
+class zero_adam_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("inv_loss_scale", ctypes.c_float), ("step", ctypes.c_int64)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m zero_sharded_mixed_flat_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_sig = {
+    "zero_plan_create": (_I, [ctypes.POINTER(_I64), _I, _I, _I, _I64, ctypes.POINTER(_P)]),
+    "zero_plan_destroy": (None, [_P]),
+    "zero_plan_info": (_I, [_P, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I),
+                            ctypes.POINTER(_I)]),
+    "zero_plan_rank": (_I, [_P, _I, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "zero_plan_unit": (_I, [_P, _I, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                            ctypes.POINTER(_I64)]),
+    "zero_plan_full_numel": (_I, [_P, ctypes.POINTER(_I64)]),
+    "zero_plan_segments": (_I, [_P, ctypes.POINTER(_I64), _I, _I, ctypes.POINTER(zero_segment), _I,
+                                ctypes.POINTER(_I)]),
+    "zero_model_state_bytes": (_I, [ctypes.c_double, _I, _I, _I, ctypes.POINTER(ctypes.c_double)]),
+    "zero_comm_volume": (_I, [ctypes.c_double, _I, _I, ctypes.POINTER(ctypes.c_double)]),
+    "zero_workspace_bytes": (_I64, [_I64, _I]),
+    "zero_reduce_shard": (_I, [ctypes.POINTER(_P), _I, _I64, _I, ctypes.c_float, _P, _P, _I64, _I, _P,
+                               _P]),
+    "zero_grad_norm": (_I, [_P, _I64, _I, ctypes.c_float, _P, _I64, _I, _P, _I, ctypes.c_float, _P, _P,
+                            _P, _P]),
+    "zero_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
+                            _P]),
+    "zero_gather_params": (_I, [_P, ctypes.POINTER(_P), _I, _I, _I, _P, _P, _I64, _P]),
+    "zero_last_error": (ctypes.c_char_p, []),
+    "zero_version": (_I, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def zero_last_error():
+    return lib.zero_last_error().decode()
+
+
+def zero_version():
+    return lib.zero_version()
+
+
+def _check(status):
+    if status != ZERO_OK:
+        raise ZeroError(status, zero_last_error())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _need(x, nbytes, what):
+    """A tensor argument must be a contiguous device tensor holding nbytes."""
+    if x is None or isinstance(x, int) or nbytes <= 0:
+        return
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes, needs {nbytes}")
+
+
+def _nbytes(x):
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        raise TypeError("pass the workspace as a tensor (or give its size explicitly)")
+    return x.numel() * x.element_size()
+
+
+def _dtype(d):
+    if isinstance(d, int):
+        return d                      # validated by the library
+    name = str(d)
+    table = {"f16": ZERO_F16, "bf16": ZERO_BF16, "torch.float16": ZERO_F16,
+             "torch.bfloat16": ZERO_BF16}
+    if name in table:
+        return table[name]
+    raise ValueError(f"not a 16-bit dtype: {d!r}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# a0: partition
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owns a ``zero_plan*``; mirrors zero_plan_* as methods."""
+
+    def __init__(self, unit_numels, nd, stage, align=8):
+        self.handle = _P()
+        sizes = (_I64 * len(unit_numels))(*[int(u) for u in unit_numels])
+        handle = _P()
+        _check(lib.zero_plan_create(sizes, len(unit_numels), int(nd), int(stage), int(align),
+                                    ctypes.byref(handle)))
+        self.handle = handle
+
+    def close(self):
+        if self.handle:
+            lib.zero_plan_destroy(self.handle)
+            self.handle = _P()
+
+    def __del__(self):
+        self.close()
+
+    def info(self):
+        a, b, c, d = _I(), _I(), _I(), _I()
+        _check(lib.zero_plan_info(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                  ctypes.byref(d)))
+        return {"n_units": a.value, "owners": b.value, "nd": c.value, "stage": d.value}
+
+    def rank(self, rank):
+        s, r = _I64(), _I64()
+        _check(lib.zero_plan_rank(self.handle, int(rank), ctypes.byref(s), ctypes.byref(r)))
+        return s.value, r.value
+
+    def unit(self, unit):
+        a, b, c, d = _I64(), _I64(), _I64(), _I64()
+        _check(lib.zero_plan_unit(self.handle, int(unit), ctypes.byref(a), ctypes.byref(b),
+                                  ctypes.byref(c), ctypes.byref(d)))
+        return a.value, b.value, c.value, d.value
+
+    def full_numel(self):
+        x = _I64()
+        _check(lib.zero_plan_full_numel(self.handle, ctypes.byref(x)))
+        return x.value
+
+    def segments(self, tensor_numels, rank):
+        sizes = (_I64 * len(tensor_numels))(*[int(t) for t in tensor_numels])
+        count = _I()
+        _check(lib.zero_plan_segments(self.handle, sizes, len(tensor_numels), int(rank), None, 0,
+                                      ctypes.byref(count)))
+        out = (zero_segment * max(count.value, 1))()
+        _check(lib.zero_plan_segments(self.handle, sizes, len(tensor_numels), int(rank), out,
+                                      count.value, ctypes.byref(count)))
+        return [(s.tensor, s.tensor_off, s.shard_off, s.len) for s in out[:count.value]]
+
+
+def zero_plan_create(unit_numels, nd, stage, align=8):
+    return Plan(unit_numels, nd, stage, align)
+
+
+# ---------------------------------------------------------------------------
+# accounting and workspace
+# ---------------------------------------------------------------------------
+
+def zero_model_state_bytes(psi, nd, stage, k_bytes=12):
+    out = ctypes.c_double()
+    _check(lib.zero_model_state_bytes(float(psi), int(nd), int(stage), int(k_bytes), ctypes.byref(out)))
+    return out.value
+
+
+def zero_comm_volume(psi, nd, stage):
+    out = ctypes.c_double()
+    _check(lib.zero_comm_volume(float(psi), int(nd), int(stage), ctypes.byref(out)))
+    return out.value
+
+
+def zero_workspace_bytes(n, n_sets):
+    b = lib.zero_workspace_bytes(int(n), int(n_sets))
+    if b < 0:
+        raise ZeroError(ZERO_EINVAL, zero_last_error())
+    return b
+
+
+# ---------------------------------------------------------------------------
+# a1-a4
+# ---------------------------------------------------------------------------
+
+def zero_reduce_shard(contribs, n, dtype, inv_loss_scale, reduced_out, workspace, set_index, flag,
+                      stream=None, workspace_bytes=None):
+    for i, c in enumerate(contribs):
+        _need(c, 2 * n, f"contribution {i}")
+    _need(reduced_out, 2 * n, "reduced_out")
+    _need(flag, 4, "flag")
+    ptrs = (_P * len(contribs))(*[_ptr(c) for c in contribs])
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(lib.zero_reduce_shard(ptrs, len(contribs), int(n), _dtype(dtype), float(inv_loss_scale),
+                                 _ptr(reduced_out), _ptr(workspace), wb, int(set_index), _ptr(flag),
+                                 _stream(stream)))
+
+
+def zero_grad_norm(grad, n, dtype, inv_loss_scale, workspace, n_sets, extra_sumsq, n_extra, max_norm,
+                   flag, norm_out, coef_out, stream=None, workspace_bytes=None):
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _need(grad, 2 * n, "grad")
+    _need(extra_sumsq, 8 * n_extra, "extra_sumsq")
+    for t, b, what in ((flag, 4, "flag"), (norm_out, 8, "norm_out"), (coef_out, 4, "coef_out")):
+        _need(t, b, what)
+    dt = _dtype(dtype) if grad is not None else 0
+    _check(lib.zero_grad_norm(_ptr(grad), int(n), dt, float(inv_loss_scale), _ptr(workspace), wb,
+                              int(n_sets), _ptr(extra_sumsq), int(n_extra), float(max_norm), _ptr(flag),
+                              _ptr(norm_out), _ptr(coef_out), _stream(stream)))
+
+
+def adam_hparams(lr, beta1, beta2, eps, weight_decay, inv_loss_scale, step):
+    return zero_adam_hparams(lr, beta1, beta2, eps, weight_decay, inv_loss_scale, int(step))
+
+
+def zero_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, flag, param_out, param_dtype,
+                   stream=None):
+    for t, b, what in ((master, 4 * n, "master"), (m, 4 * n, "m"), (v, 4 * n, "v"),
+                       (grad, 2 * n, "grad"), (param_out, 2 * n, "param_out"), (coef, 4, "coef"),
+                       (flag, 4, "flag")):
+        _need(t, b, what)
+    _check(lib.zero_adam_step(_ptr(master), _ptr(m), _ptr(v), _ptr(grad), _dtype(grad_dtype), int(n),
+                              ctypes.byref(hp), _ptr(coef), _ptr(flag), _ptr(param_out),
+                              _dtype(param_dtype), _stream(stream)))
+
+
+def zero_gather_params(plan, shards, unit_begin, unit_end, dtype, full, workspace=None, stream=None,
+                       workspace_bytes=None):
+    ptrs = (_P * len(shards))(*[_ptr(s) for s in shards])
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    handle = plan.handle if isinstance(plan, Plan) else plan
+    if isinstance(plan, Plan):
+        info = plan.info()
+        if len(shards) != info["owners"]:
+            raise ValueError(f"need {info['owners']} shards, got {len(shards)}")
+        shard_numel, _ = plan.rank(0)
+        for i, sh in enumerate(shards):
+            _need(sh, 2 * shard_numel, f"shard {i}")
+        _need(full, 2 * plan.full_numel(), "full")
+    _check(lib.zero_gather_params(handle, ptrs, int(unit_begin), int(unit_end), _dtype(dtype),
+                                  _ptr(full), _ptr(workspace), wb, _stream(stream)))

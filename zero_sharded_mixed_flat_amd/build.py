@@ -1,0 +1,52 @@
+"""Build ``lib/libzero_flat.so`` for gfx950 with hipcc.
+
+Usage: ``python -m zero_sharded_mixed_flat_amd.build`` (or ``build()``).  Always
+recompiles.  The host partitioner is plain C++; the kernels are HIP for gfx950
+only.  Packed fp32 instructions are disabled on the device side.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIBDIR = os.path.join(HERE, "lib")
+LIB = os.path.join(LIBDIR, "libzero_flat.so")
+ARCH = "gfx950"
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose=True):
+    hipcc = _hipcc()
+    os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+    plan_o = os.path.join(objdir, "plan.o")
+    kern_o = os.path.join(objdir, "kernels.o")
+    _run([hipcc, *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
+    _run([hipcc, *common, "-x", "hip", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", plan_o, kern_o, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,225 @@
+// Host side of the library: the flat-bucket partitioner, the model-state and
+// communication accounting, the workspace size and the error channel.
+//
+// Partition (L18 notes §2.1, §3.2 and exercise 6; Illustrated ZeRO §8.4):
+// Adam is elementwise, so the flat parameter vector is cut into equal
+// contiguous pieces, one per data-parallel rank, and a tensor may straddle two
+// ranks.  Stage 3 partitions each unit (layer) on its own so that one layer can
+// be gathered into a contiguous buffer.  All arithmetic here is int64.
+
+#include <algorithm>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace zf {
+
+namespace {
+thread_local std::string g_error;
+}  // namespace
+
+int fail(int code, const std::string& msg) {
+    g_error = msg;
+    return code;
+}
+
+int ok() {
+    g_error.clear();
+    return ZERO_OK;
+}
+
+int64_t partial_blocks(int64_t n) {
+    // One block per 256 16-byte vectors, at least 1, at most kMaxPartialBlocks.
+    int64_t vecs = (n + 7) / 8;
+    int64_t b = (vecs + kBlock - 1) / kBlock;
+    if (b < 1) b = 1;
+    if (b > kMaxPartialBlocks) b = kMaxPartialBlocks;
+    return b;
+}
+
+}  // namespace zf
+
+extern "C" {
+
+const char* zero_last_error(void) { return zf::g_error.c_str(); }
+
+int zero_version(void) { return 10000; }
+
+int zero_plan_create(const int64_t* unit_numels, int n_units, int nd, int stage,
+                     int64_t align_elems, zero_plan** out) {
+    if (out == nullptr) return zf::fail(ZERO_EINVAL, "zero_plan_create: out is NULL");
+    *out = nullptr;
+    if (unit_numels == nullptr || n_units < 1)
+        return zf::fail(ZERO_EINVAL, "zero_plan_create: need at least one unit");
+    if (nd < 1 || nd > ZERO_MAX_RANKS)
+        return zf::fail(ZERO_EINVAL, "zero_plan_create: nd must be in [1, 1024]");
+    if (stage < 0 || stage > 3)
+        return zf::fail(ZERO_EINVAL, "zero_plan_create: stage must be 0, 1, 2 or 3");
+    if (align_elems < 1 || align_elems > (int64_t(1) << 30))
+        return zf::fail(ZERO_EINVAL, "zero_plan_create: align must be in [1, 2^30]");
+    int64_t total = 0;
+    for (int i = 0; i < n_units; ++i) {
+        if (unit_numels[i] < 0) return zf::fail(ZERO_EINVAL, "zero_plan_create: negative unit size");
+        if (unit_numels[i] > (int64_t(1) << 50) - total)
+            return zf::fail(ZERO_EINVAL, "zero_plan_create: more than 2^50 elements");
+        total += unit_numels[i];
+    }
+    if (total == 0) return zf::fail(ZERO_EINVAL, "zero_plan_create: no elements");
+
+    zero_plan* p = new (std::nothrow) zero_plan;
+    if (p == nullptr) return zf::fail(ZERO_ENOMEM, "zero_plan_create: out of host memory");
+    p->nd = nd;
+    p->stage = stage;
+    p->owners = stage == 0 ? 1 : nd;
+    p->align = align_elems;
+    std::vector<int64_t> sizes;
+    if (stage == 3)
+        sizes.assign(unit_numels, unit_numels + n_units);
+    else
+        sizes.push_back(total);
+    int64_t full_base = 0, shard_base = 0;
+    try {
+        for (int64_t u : sizes) {
+            int64_t per = (u + p->owners - 1) / p->owners;
+            int64_t s = (per + align_elems - 1) / align_elems * align_elems;
+            p->units.push_back({u, s, full_base, shard_base});
+            full_base += int64_t(p->owners) * s;
+            shard_base += s;
+        }
+    } catch (const std::bad_alloc&) {
+        delete p;
+        return zf::fail(ZERO_ENOMEM, "zero_plan_create: out of host memory");
+    }
+    p->shard_numel = shard_base;
+    p->full_numel = full_base;
+    *out = p;
+    return zf::ok();
+}
+
+void zero_plan_destroy(zero_plan* plan) { delete plan; }
+
+int zero_plan_info(const zero_plan* plan, int* n_units, int* owners, int* nd, int* stage) {
+    if (plan == nullptr) return zf::fail(ZERO_EINVAL, "zero_plan_info: plan is NULL");
+    if (n_units) *n_units = int(plan->units.size());
+    if (owners) *owners = plan->owners;
+    if (nd) *nd = plan->nd;
+    if (stage) *stage = plan->stage;
+    return zf::ok();
+}
+
+int zero_plan_rank(const zero_plan* plan, int rank, int64_t* shard_numel, int64_t* real_numel) {
+    if (plan == nullptr) return zf::fail(ZERO_EINVAL, "zero_plan_rank: plan is NULL");
+    if (rank < 0 || rank >= plan->nd) return zf::fail(ZERO_EINVAL, "zero_plan_rank: rank out of range");
+    int r = plan->owners == 1 ? 0 : rank;
+    int64_t real = 0;
+    for (const auto& u : plan->units) {
+        int64_t lo = std::min(int64_t(r) * u.slice_numel, u.numel);
+        int64_t hi = std::min(int64_t(r + 1) * u.slice_numel, u.numel);
+        real += hi - lo;
+    }
+    if (shard_numel) *shard_numel = plan->shard_numel;
+    if (real_numel) *real_numel = real;
+    return zf::ok();
+}
+
+int zero_plan_unit(const zero_plan* plan, int unit, int64_t* numel, int64_t* slice_numel,
+                   int64_t* full_base, int64_t* shard_base) {
+    if (plan == nullptr) return zf::fail(ZERO_EINVAL, "zero_plan_unit: plan is NULL");
+    if (unit < 0 || unit >= int(plan->units.size()))
+        return zf::fail(ZERO_EINVAL, "zero_plan_unit: unit out of range");
+    const auto& u = plan->units[unit];
+    if (numel) *numel = u.numel;
+    if (slice_numel) *slice_numel = u.slice_numel;
+    if (full_base) *full_base = u.full_base;
+    if (shard_base) *shard_base = u.shard_base;
+    return zf::ok();
+}
+
+int zero_plan_full_numel(const zero_plan* plan, int64_t* padded) {
+    if (plan == nullptr || padded == nullptr)
+        return zf::fail(ZERO_EINVAL, "zero_plan_full_numel: NULL argument");
+    *padded = plan->full_numel;
+    return zf::ok();
+}
+
+int zero_plan_segments(const zero_plan* plan, const int64_t* tensor_numels, int n_tensors, int rank,
+                       zero_segment* out, int cap, int* count) {
+    if (plan == nullptr || count == nullptr || (n_tensors > 0 && tensor_numels == nullptr))
+        return zf::fail(ZERO_EINVAL, "zero_plan_segments: NULL argument");
+    if (n_tensors < 0 || cap < 0 || (cap > 0 && out == nullptr))
+        return zf::fail(ZERO_EINVAL, "zero_plan_segments: bad count or capacity");
+    if (rank < 0 || rank >= plan->nd) return zf::fail(ZERO_EINVAL, "zero_plan_segments: rank out of range");
+    // Validate that the tensors fill the units exactly, before writing anything.
+    {
+        size_t ui = 0;
+        int64_t pos = 0, sum = 0;
+        for (int t = 0; t < n_tensors; ++t) {
+            int64_t len = tensor_numels[t];
+            if (len < 0) return zf::fail(ZERO_EINVAL, "zero_plan_segments: negative tensor size");
+            if (len == 0) continue;
+            while (ui < plan->units.size() && pos == plan->units[ui].numel) { ++ui; pos = 0; }
+            if (ui >= plan->units.size() || len > plan->units[ui].numel - pos)
+                return zf::fail(ZERO_EINVAL, "zero_plan_segments: tensors do not fill the units");
+            pos += len;
+            sum += len;
+        }
+        int64_t psi = 0;
+        for (const auto& u : plan->units) psi += u.numel;
+        if (sum != psi) return zf::fail(ZERO_EINVAL, "zero_plan_segments: tensor sizes do not add up");
+    }
+    int r = plan->owners == 1 ? 0 : rank;
+    int written = 0;
+    size_t ui = 0;
+    int64_t pos = 0;
+    for (int t = 0; t < n_tensors; ++t) {
+        int64_t len = tensor_numels[t];
+        if (len == 0) continue;
+        while (pos == plan->units[ui].numel) { ++ui; pos = 0; }
+        const auto& u = plan->units[ui];
+        int64_t lo = std::min(int64_t(r) * u.slice_numel, u.numel);
+        int64_t hi = std::min(int64_t(r + 1) * u.slice_numel, u.numel);
+        int64_t a = std::max(lo, pos), b = std::min(hi, pos + len);
+        if (a < b) {
+            if (written < cap)
+                out[written] = {t, a - pos, u.shard_base + (a - int64_t(r) * u.slice_numel), b - a};
+            ++written;
+        }
+        pos += len;
+    }
+    *count = written;
+    return zf::ok();
+}
+
+int zero_model_state_bytes(double psi, int nd, int stage, int k_bytes, double* out) {
+    if (out == nullptr || nd < 1 || !(psi >= 0) || k_bytes < 0)
+        return zf::fail(ZERO_EINVAL, "zero_model_state_bytes: bad argument");
+    double k = k_bytes;
+    switch (stage) {
+        case 0: *out = psi * (4.0 + k); break;
+        case 1: *out = psi * (4.0 + k / nd); break;
+        case 2: *out = psi * (2.0 + (2.0 + k) / nd); break;
+        case 3: *out = psi * ((4.0 + k) / nd); break;
+        default: return zf::fail(ZERO_EINVAL, "zero_model_state_bytes: stage must be 0..3");
+    }
+    return zf::ok();
+}
+
+int zero_comm_volume(double psi, int nd, int stage, double* elems_sent) {
+    if (elems_sent == nullptr || nd < 1 || !(psi >= 0) || stage < 0 || stage > 3)
+        return zf::fail(ZERO_EINVAL, "zero_comm_volume: bad argument");
+    double passes = stage == 3 ? 3.0 : 2.0;
+    *elems_sent = passes * psi * double(nd - 1) / double(nd);
+    return zf::ok();
+}
+
+int64_t zero_workspace_bytes(int64_t n, int n_sets) {
+    if (n < 0 || n_sets < 0 || n_sets > ZERO_MAX_RANKS) {
+        zf::fail(ZERO_EINVAL, "zero_workspace_bytes: bad argument");
+        return -1;
+    }
+    zf::ok();
+    return zf::kTableBytes + int64_t(n_sets) * zf::partial_blocks(n) * int64_t(sizeof(double));
+}
+
+}  // extern "C"

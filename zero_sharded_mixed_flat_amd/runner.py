@@ -1,0 +1,203 @@
+"""One rank's ZeRO step over a workload, as a sequence of C-ABI calls.
+
+``RankStep`` allocates the device buffers a workload needs (caller-owned, as
+the ABI requires), fills them from the seeded generators, and runs steps:
+
+    flag = 0
+    reduce each emulated owner's slice            zero_reduce_shard   (a1)
+    norm + clip multiplier over all owners        zero_grad_norm      (a2)
+    AdamW + 16-bit cast into the parameter buffer zero_adam_step      (a3)
+    per-unit gather of every rank's 16-bit shard  zero_gather_params  (a4)
+
+All calls go to one stream with no host synchronisation inside a step: the
+clip multiplier and the skip flag stay in device memory.  Contributions of the
+emulated ranks are buffers in this GPU's memory (one process, one GPU).
+"""
+
+import torch
+
+from . import abi, synth
+
+TORCH16 = synth.TORCH_DTYPES
+
+
+class RankStep:
+    def __init__(self, w, seed=0, device="cuda", tile_period=None, contrib_layout="auto"):
+        self.w = w
+        self.seed = seed
+        self.device = device
+        self.t = 1
+        self.plan = abi.Plan(w.units, w.nd, w.stage, w.align)
+        self.n, _ = self.plan.rank(0)
+        self.full_numel = self.plan.full_numel()
+        info = self.plan.info()
+        self.n_units = info["n_units"]
+        self.owners = list(range(w.nd)) if w.all_ranks else [w.rank]
+        gdt, pdt = TORCH16[w.grad_dtype], TORCH16[w.param_dtype]
+        n = self.n
+        dev = device
+
+        # Gradients.  With every rank emulated on one flat unit, each rank holds a
+        # full local gradient and owner o's contribution from rank r is the slice
+        # [o*n, (o+1)*n) of rank r's gradient.  Otherwise only the owned slice of
+        # each rank's gradient exists, as an [nd, n] block in shard order.
+        self.local = None
+        self.contrib_block = None
+        if w.pre_reduced:
+            self.grad = synth.grad16(n, w.grad_dtype, w.grad_std * w.loss_scale, seed, 1, dev)
+            if tile_period:
+                synth.tile_(self.grad, tile_period)
+        elif w.all_ranks and self.n_units == 1:
+            self.local = torch.empty((w.nd, self.full_numel), dtype=gdt, device=dev)
+            self.fresh_gradients(step=0, tile_period=tile_period)
+        else:
+            self.contrib_block = torch.empty((w.nd, n), dtype=gdt, device=dev)
+            for r in range(w.nd):
+                synth.normal_(self.contrib_block[r], w.grad_std * w.loss_scale, seed, 100 + r)
+                synth.outliers_(self.contrib_block[r], w.outlier_frac, w.outlier_mult, seed, 100 + r)
+                if tile_period:
+                    synth.tile_(self.contrib_block[r], tile_period)
+        if not w.pre_reduced:
+            self.reduced = torch.empty((len(self.owners), n), dtype=gdt, device=dev)
+
+        # fp32 optimizer state, one shard per emulated owner.
+        k = len(self.owners)
+        self.master = torch.empty((k, n), dtype=torch.float32, device=dev)
+        self.m = torch.empty((k, n), dtype=torch.float32, device=dev)
+        self.v = torch.empty((k, n), dtype=torch.float32, device=dev)
+        for i, o in enumerate(self.owners):
+            synth.normal_(self.master[i], w.master_std, seed, 200 + o)
+            if w.m_std:
+                synth.normal_(self.m[i], w.m_std, seed, 300 + o)
+            else:
+                self.m[i].zero_()
+            if w.v_std:
+                synth.abs_normal_(self.v[i], w.v_std, seed, 400 + o)
+            else:
+                self.v[i].zero_()
+            if w.all_ranks:
+                self._zero_padding(o, self.master[i])
+
+        # 16-bit parameters.  ZeRO-1/2 write the owner's slice straight into the
+        # full gather buffer; ZeRO-3 writes the owner's shard, then gathers every
+        # rank's shard unit by unit; a pre-reduced owner update writes its shard.
+        self.full = None
+        self.shards = None
+        if w.gather_per_unit:
+            self.shards = torch.empty((w.nd, n), dtype=pdt, device=dev)
+            for r in range(w.nd):
+                if r not in self.owners:
+                    synth.normal_(self.shards[r], w.gather_shard_std, seed, 500 + r)
+            self.full = torch.zeros(self.full_numel, dtype=pdt, device=dev)
+        elif w.pre_reduced:
+            self.param = torch.zeros(n, dtype=pdt, device=dev)
+        else:
+            self.full = torch.zeros(self.full_numel, dtype=pdt, device=dev)
+
+        n_sets = 1 if w.pre_reduced else len(self.owners)
+        self.ws = torch.empty(abi.zero_workspace_bytes(n, n_sets), dtype=torch.uint8, device=dev)
+        self.n_sets = n_sets
+        self.flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.norm = torch.zeros(1, dtype=torch.float64, device=dev)
+        self.coef = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    # -- inputs --------------------------------------------------------------
+
+    def _zero_padding(self, owner, t):
+        """Zero the padded tail of an emulated owner's single-unit shard."""
+        if self.n_units != 1:
+            return
+        numel, s, _, _ = self.plan.unit(0)
+        real = max(0, min(numel - owner * s, s))
+        t[real:].zero_()
+
+    def fresh_gradients(self, step, tile_period=None):
+        """Draw every emulated rank's full local gradient for ``step`` (padding zero)."""
+        w = self.w
+        psi = w.psi
+        for r in range(w.nd):
+            g = self.local[r]
+            synth.normal_(g[:psi], w.grad_std * w.loss_scale, self.seed, 1000 * (step + 1) + r)
+            synth.outliers_(g[:psi], w.outlier_frac, w.outlier_mult, self.seed, 1000 * (step + 1) + r)
+            if tile_period:
+                synth.tile_(g[:psi], tile_period)
+            g[psi:].zero_()
+
+    def contribs(self, i):
+        """Device views of the nd contributions to emulated owner i's slice."""
+        o = self.owners[i]
+        if self.local is not None:
+            return [self.local[r, o * self.n:(o + 1) * self.n] for r in range(self.w.nd)]
+        return [self.contrib_block[r] for r in range(self.w.nd)]
+
+    def param_out(self, i):
+        o = self.owners[i]
+        if self.shards is not None:
+            return self.shards[o]
+        if self.w.pre_reduced:
+            return self.param
+        return self.full[o * self.n:(o + 1) * self.n]
+
+    def grad_of(self, i):
+        return self.grad if self.w.pre_reduced else self.reduced[i]
+
+    # -- the step ------------------------------------------------------------
+
+    def hparams(self):
+        w = self.w
+        return abi.adam_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.inv_loss_scale, self.t)
+
+    def reduce_all(self, stream=None):
+        for i in range(len(self.owners)):
+            abi.zero_reduce_shard(self.contribs(i), self.n, self.w.grad_dtype, self.w.inv_loss_scale,
+                                  self.reduced[i], self.ws, i, self.flag, stream)
+
+    def norm_all(self, stream=None):
+        w = self.w
+        grad = self.grad if w.pre_reduced else None
+        abi.zero_grad_norm(grad, self.n, w.grad_dtype, w.inv_loss_scale, self.ws, self.n_sets, None, 0,
+                           w.max_norm, self.flag, self.norm, self.coef, stream)
+
+    def adam_all(self, stream=None):
+        w = self.w
+        hp = self.hparams()
+        for i in range(len(self.owners)):
+            abi.zero_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype, self.n,
+                               hp, self.coef, self.flag, self.param_out(i), w.param_dtype, stream)
+
+    def gather_unit(self, u, stream=None):
+        abi.zero_gather_params(self.plan, list(self.shards), u, u + 1, self.w.param_dtype, self.full,
+                               self.ws, stream)
+
+    def gather_all(self, stream=None):
+        for u in range(self.n_units):
+            self.gather_unit(u, stream)
+
+    def step(self, stream=None):
+        """Enqueue one whole step; returns without synchronising."""
+        self.flag.zero_()
+        if not self.w.pre_reduced:
+            self.reduce_all(stream)
+        self.norm_all(stream)
+        self.adam_all(stream)
+        if self.shards is not None:
+            self.gather_all(stream)
+        self.t += 1
+
+    # -- accounting ------------------------------------------------------------
+
+    def algorithmic_bytes(self):
+        """Bytes the step must move per the method (not counting re-reads).
+
+        Per owned element: 2*Nd (contributions) + 2 (write reduced) + 2 (read
+        reduced) + 24 (read and write master, m, v) + 2 (write the 16-bit
+        parameter); 30 bytes when the gradient arrives reduced (2 to read it for
+        the norm, 2 to read it again in Adam, ...).  A ZeRO-3 gather adds 4
+        bytes (read + write) per gathered element.
+        """
+        w = self.w
+        per = 30 if w.pre_reduced else 2 * w.nd + 30
+        total = per * self.n * len(self.owners)
+        if self.shards is not None:
+            total += 4 * self.n * w.nd
+        return total
