@@ -201,6 +201,8 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
  * bitwise repeatable: the summation tree depends only on n and n_sets.
  *
  * n is the per-set shard length used by the producing launches; 1 <= n_sets.
+ * With n = 0 no partial sum is read (they are all zero) and grad may be NULL
+ * or not: norm = sqrt(sum of extra_sumsq).
  */
 int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
                    void* workspace, int64_t workspace_bytes, int n_sets,

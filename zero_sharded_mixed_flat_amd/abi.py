@@ -10,6 +10,11 @@ if the shared library is missing, importing this module fails.
 import ctypes
 import os
 
+# torch brings its own HIP runtime.  Load it BEFORE the library so that the
+# library's libamdhip64.so.7 dependency resolves to that same copy: two HIP
+# runtimes in one process each open the device, and the second one sees none.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "lib", "libzero_flat.so")
 

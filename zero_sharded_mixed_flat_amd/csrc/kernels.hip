@@ -27,6 +27,8 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <tuple>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -408,43 +410,56 @@ unsigned grid_for(int64_t work_items, int64_t max_blocks) {
     return unsigned(b);
 }
 
-int launch_status(const char* where) {
-    hipError_t e = hipGetLastError();
+int hip_status(hipError_t e, const char* where) {
     if (e != hipSuccess) return fail(ZERO_EHIP, std::string(where) + ": " + hipGetErrorString(e));
     return ok();
 }
 
+// Launches `kernel` and returns the status of THIS launch.  hipGetLastError()
+// is not used: it also reports earlier failures of other libraries' calls on
+// this thread.  The arguments are converted to the kernel's parameter types.
+template <typename... KArgs, typename... Actual>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Actual&&... a) {
+    static_assert(sizeof...(KArgs) == sizeof...(Actual), "argument count");
+    std::tuple<KArgs...> args(std::forward<Actual>(a)...);
+    return std::apply(
+        [&](auto&... x) {
+            void* argv[] = {static_cast<void*>(&x)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+        },
+        args);
+}
+
 template <int DT>
-void launch_reduce(int nd, dim3 grid, hipStream_t s, const Ptrs64& tab, const uint16_t* const* dtab,
-                   Span sp, float inv_nd, float nd_f, int pow2, float inv_s, uint16_t* out,
-                   double* partials, int32_t* flag) {
-#define ZF_REDUCE(ND_)                                                                          \
-    hipLaunchKernelGGL((reduce_kernel<DT, ND_>), grid, dim3(kBlock), 0, s, tab, dtab, nd, sp, \
-                       inv_nd, nd_f, pow2, inv_s, out, partials, flag)
+hipError_t launch_reduce(int nd, dim3 grid, hipStream_t s, const Ptrs64& tab,
+                         const uint16_t* const* dtab, Span sp, float inv_nd, float nd_f, int pow2,
+                         float inv_s, uint16_t* out, double* partials, int32_t* flag) {
+#define ZF_REDUCE(ND_)                                                                             \
+    return launch(reduce_kernel<DT, ND_>, grid, dim3(kBlock), s, tab, dtab, nd, sp, inv_nd, nd_f, \
+                  pow2, inv_s, out, partials, flag)
     switch (dtab ? -1 : nd) {
-        case -1: ZF_REDUCE(-1); break;
-        case 1: ZF_REDUCE(1); break;
-        case 2: ZF_REDUCE(2); break;
-        case 4: ZF_REDUCE(4); break;
-        case 8: ZF_REDUCE(8); break;
-        case 16: ZF_REDUCE(16); break;
-        case 32: ZF_REDUCE(32); break;
-        case 64: ZF_REDUCE(64); break;
-        default: ZF_REDUCE(0); break;
+        case -1: ZF_REDUCE(-1);
+        case 1: ZF_REDUCE(1);
+        case 2: ZF_REDUCE(2);
+        case 4: ZF_REDUCE(4);
+        case 8: ZF_REDUCE(8);
+        case 16: ZF_REDUCE(16);
+        case 32: ZF_REDUCE(32);
+        case 64: ZF_REDUCE(64);
+        default: ZF_REDUCE(0);
     }
 #undef ZF_REDUCE
 }
 
 template <int GDT>
-void launch_adam(int pdt, dim3 grid, hipStream_t s, float* master, float* m, float* v,
-                 const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
-                 const int32_t* flag, uint16_t* param) {
+hipError_t launch_adam(int pdt, dim3 grid, hipStream_t s, float* master, float* m, float* v,
+                       const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
+                       const int32_t* flag, uint16_t* param) {
     if (pdt == ZERO_F16)
-        hipLaunchKernelGGL((adam_kernel<GDT, ZERO_F16>), grid, dim3(kBlock), 0, s, master, m, v,
-                           grad, sp, c, coef, flag, param);
-    else
-        hipLaunchKernelGGL((adam_kernel<GDT, ZERO_BF16>), grid, dim3(kBlock), 0, s, master, m, v,
-                           grad, sp, c, coef, flag, param);
+        return launch(adam_kernel<GDT, ZERO_F16>, grid, dim3(kBlock), s, master, m, v, grad, sp, c,
+                      coef, flag, param);
+    return launch(adam_kernel<GDT, ZERO_BF16>, grid, dim3(kBlock), s, master, m, v, grad, sp, c, coef,
+                  flag, param);
 }
 
 constexpr int64_t kMaxAdamBlocks = 2048;
@@ -506,8 +521,8 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
         // The runtime stages a pageable source before returning, so `ptrs`
         // may go out of scope once the call is back.
         dtab = static_cast<const uint16_t* const*>(workspace);
-        if (hipMemcpyAsync(workspace, ptrs.data(), sizeof(void*) * nd, hipMemcpyHostToDevice, s) != hipSuccess)
-            return launch_status(fn);
+        const hipError_t e = hipMemcpyAsync(workspace, ptrs.data(), sizeof(void*) * nd, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, fn);
     }
     std::vector<const void*> all16(ptrs);
     all16.push_back(reduced_out);
@@ -516,13 +531,13 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
     const bool pow2 = std::frexp(double(nd), &e2) == 0.5;
     const float inv_nd = pow2 ? 1.0f / float(nd) : 0.0f;
     const dim3 grid{unsigned(blocks)};
-    if (dtype == ZERO_F16)
-        launch_reduce<ZERO_F16>(nd, grid, s, tab, dtab, sp, inv_nd, float(nd), pow2, inv_loss_scale,
-                                static_cast<uint16_t*>(reduced_out), partials, flag);
-    else
-        launch_reduce<ZERO_BF16>(nd, grid, s, tab, dtab, sp, inv_nd, float(nd), pow2, inv_loss_scale,
-                                 static_cast<uint16_t*>(reduced_out), partials, flag);
-    return launch_status(fn);
+    const hipError_t e =
+        dtype == ZERO_F16
+            ? launch_reduce<ZERO_F16>(nd, grid, s, tab, dtab, sp, inv_nd, float(nd), pow2, inv_loss_scale,
+                                      static_cast<uint16_t*>(reduced_out), partials, flag)
+            : launch_reduce<ZERO_BF16>(nd, grid, s, tab, dtab, sp, inv_nd, float(nd), pow2, inv_loss_scale,
+                                       static_cast<uint16_t*>(reduced_out), partials, flag);
+    return hip_status(e, fn);
 }
 
 int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale, void* workspace,
@@ -556,22 +571,24 @@ int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t blocks = partial_blocks(n);
     double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kTableBytes);
-    if (grad != nullptr) {
+    if (grad != nullptr && n > 0) {
         const void* p16[1] = {grad};
         const Span sp = n > 0 ? make_span(n, p16, 1, nullptr, 0) : Span{0, 0, 0};
-        if (dtype == ZERO_F16)
-            hipLaunchKernelGGL((sumsq_kernel<ZERO_F16>), dim3(unsigned(blocks)), dim3(kBlock), 0, s,
-                               static_cast<const uint16_t*>(grad), sp, inv_loss_scale, partials, flag);
-        else
-            hipLaunchKernelGGL((sumsq_kernel<ZERO_BF16>), dim3(unsigned(blocks)), dim3(kBlock), 0, s,
-                               static_cast<const uint16_t*>(grad), sp, inv_loss_scale, partials, flag);
-        int st = launch_status(fn);
-        if (st != ZERO_OK) return st;
+        const uint16_t* g16 = static_cast<const uint16_t*>(grad);
+        const hipError_t e =
+            dtype == ZERO_F16
+                ? launch(sumsq_kernel<ZERO_F16>, dim3(unsigned(blocks)), dim3(kBlock), s, g16, sp,
+                         inv_loss_scale, partials, flag)
+                : launch(sumsq_kernel<ZERO_BF16>, dim3(unsigned(blocks)), dim3(kBlock), s, g16, sp,
+                         inv_loss_scale, partials, flag);
+        if (e != hipSuccess) return hip_status(e, fn);
     }
-    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kFinalizeBlock), 0, s, partials,
-                       int64_t(n_sets) * blocks, extra_sumsq, n_extra, max_norm, flag, norm_out,
-                       coef_out);
-    return launch_status(fn);
+    // With n = 0 every partial sum is zero by definition: none is read, so an
+    // empty gradient needs no partials pass and no earlier launch.
+    const int64_t count = n > 0 ? int64_t(n_sets) * blocks : 0;
+    return hip_status(launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), s, partials, count,
+                             extra_sumsq, n_extra, max_norm, flag, norm_out, coef_out),
+                      fn);
 }
 
 int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
@@ -630,13 +647,13 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
     const Span sp = make_span(n, p16, 2, p32, 3);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(grid_for(sp.nvec > 0 ? sp.nvec : n, kMaxAdamBlocks));
-    if (grad_dtype == ZERO_F16)
-        launch_adam<ZERO_F16>(param_dtype, grid, s, master, m, v, static_cast<const uint16_t*>(grad), sp, c,
-                              coef_dev, flag, static_cast<uint16_t*>(param_out));
-    else
-        launch_adam<ZERO_BF16>(param_dtype, grid, s, master, m, v, static_cast<const uint16_t*>(grad), sp, c,
-                               coef_dev, flag, static_cast<uint16_t*>(param_out));
-    return launch_status(fn);
+    const uint16_t* g16 = static_cast<const uint16_t*>(grad);
+    uint16_t* p16o = static_cast<uint16_t*>(param_out);
+    const hipError_t e =
+        grad_dtype == ZERO_F16
+            ? launch_adam<ZERO_F16>(param_dtype, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o)
+            : launch_adam<ZERO_BF16>(param_dtype, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o);
+    return hip_status(e, fn);
 }
 
 int zero_gather_params(const zero_plan* plan, const void* const* shards, int unit_begin, int unit_end,
@@ -673,8 +690,8 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
     for (int r = 0; r < owners; ++r) aligned = aligned && (addr(shards[r]) & 15) == 0;
     if (device_table) {
         dtab = static_cast<const uint16_t* const*>(workspace);
-        if (hipMemcpyAsync(workspace, shards, sizeof(void*) * owners, hipMemcpyHostToDevice, s) != hipSuccess)
-            return launch_status(fn);
+        const hipError_t e = hipMemcpyAsync(workspace, shards, sizeof(void*) * owners, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, fn);
     } else {
         for (int r = 0; r < owners; ++r) tab.p[r] = static_cast<const uint16_t*>(shards[r]);
     }
@@ -684,14 +701,13 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
         const int vec = aligned ? 1 : 0;
         const int64_t items = vec ? ui.slice_numel / 8 : ui.slice_numel;
         const dim3 grid(grid_for(items, kMaxGatherBlocksX), unsigned(owners));
-        if (device_table)
-            hipLaunchKernelGGL(gather_kernel<true>, grid, dim3(kBlock), 0, s, tab, dtab, ui.slice_numel,
-                               ui.shard_base, ui.full_base, vec, static_cast<uint16_t*>(full));
-        else
-            hipLaunchKernelGGL(gather_kernel<false>, grid, dim3(kBlock), 0, s, tab, dtab, ui.slice_numel,
-                               ui.shard_base, ui.full_base, vec, static_cast<uint16_t*>(full));
-        int st = launch_status(fn);
-        if (st != ZERO_OK) return st;
+        uint16_t* f16 = static_cast<uint16_t*>(full);
+        const hipError_t e =
+            device_table ? launch(gather_kernel<true>, grid, dim3(kBlock), s, tab, dtab, ui.slice_numel,
+                                  ui.shard_base, ui.full_base, vec, f16)
+                         : launch(gather_kernel<false>, grid, dim3(kBlock), s, tab, dtab, ui.slice_numel,
+                                  ui.shard_base, ui.full_base, vec, f16);
+        if (e != hipSuccess) return hip_status(e, fn);
     }
     return ok();
 }
