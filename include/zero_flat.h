@@ -143,9 +143,9 @@ int zero_comm_volume(double psi, int nd, int stage, double* elems_sent);
 
 /*
  * Bytes of device workspace for `n_sets` partial-sum sets over shards of n
- * elements.  The workspace holds, per set, the fp64 sums of squares of one
- * reduce (or partials) launch, plus a table of up to ZERO_MAX_RANKS device
- * pointers.  The caller allocates it (any alignment >= 8) and passes it to
+ * elements.  The workspace holds a table of up to ZERO_MAX_RANKS device
+ * pointers, 1024 second-level fp64 sums for the norm, and per set the fp64
+ * sums of squares of one reduce (or partials) launch (one per 2048 elements).  The caller allocates it (any alignment >= 8) and passes it to
  * zero_reduce_shard / zero_grad_norm / zero_gather_params; its contents need no
  * initialisation.  Returns -1 on bad arguments.
  */

@@ -97,9 +97,14 @@ def test_plan_rejects_bad_arguments():
 
 
 def test_workspace_bytes():
-    assert abi.zero_workspace_bytes(0, 0) == 8192
-    assert abi.zero_workspace_bytes(8 * 256, 1) == 8192 + 8
-    assert abi.zero_workspace_bytes(10 ** 10, 2) == 8192 + 2 * 2048 * 8
+    # 8 KiB pointer table + 8 KiB of second-level sums + one fp64 partial sum
+    # per 2048 elements and set (at least one per set).
+    base = 16384
+    assert abi.zero_workspace_bytes(0, 0) == base
+    assert abi.zero_workspace_bytes(0, 1) == base + 8
+    assert abi.zero_workspace_bytes(2048, 1) == base + 8
+    assert abi.zero_workspace_bytes(2049, 3) == base + 3 * 2 * 8
+    assert abi.zero_workspace_bytes(10 ** 10, 2) == base + 2 * (-(-10 ** 10 // 2048)) * 8
     with pytest.raises(abi.ZeroError):
         abi.zero_workspace_bytes(-1, 1)
 

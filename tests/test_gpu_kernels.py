@@ -200,8 +200,34 @@ def test_reduce_is_deterministic(abi):
         abi.zero_reduce_shard(dev, n, "bf16", 1.0, out, ws, 0, flag)
         abi.zero_grad_norm(None, n, "bf16", 1.0, ws, 1, None, 0, 1.0, flag, norm, coef)
         torch.cuda.synchronize()
-        norms.append((norm.item(), ws.cpu().numpy().tobytes()[8192:]))
+        norms.append((norm.item(), ws.cpu().numpy().tobytes()[16384:]))   # partial sums
     assert norms[0] == norms[1] == norms[2]
+
+
+@pytest.mark.parametrize("n, sets", [(20_000_003, 1), (5_000_001, 4)])
+def test_norm_two_stage_finalize(abi, n, sets):
+    # More than 8192 partial sums: the finalize folds them in two stages.
+    _note(f"two-stage norm n={n} sets={sets}")
+    rng = np.random.default_rng(n + sets)
+    grads = [_rand16(rng, n, 1e-3, "bf16") for _ in range(sets)]
+    ws = _ws(abi, n, sets)
+    flag, norm, coef = _scalars()
+    outs = []
+    for i, g in enumerate(grads):
+        out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        abi.zero_reduce_shard([_dev16(g, "bf16")], n, "bf16", 1.0, out, ws, i, flag)
+        outs.append(out)
+    abi.zero_grad_norm(None, n, "bf16", 1.0, ws, sets, None, 0, 1.0, flag, norm, coef)
+    torch.cuda.synchronize()
+    first = norm.item()
+    abi.zero_grad_norm(None, n, "bf16", 1.0, ws, sets, None, 0, 1.0, flag, norm, coef)
+    torch.cuda.synchronize()
+    assert norm.item() == first                                   # same tree every time
+    ref = step.norm_from_sumsq(sum(step.sumsq_exact(g, "bf16") for g in grads))
+    assert first == pytest.approx(ref, rel=1e-5)
+    assert abs(first - ref) <= 1e-12 * ref
+    for g, out in zip(grads, outs):
+        assert np.array_equal(_bits(out), g)                      # nd = 1 is the identity
 
 
 # ---------------------------------------------------------------------------

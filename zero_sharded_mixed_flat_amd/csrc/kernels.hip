@@ -3,11 +3,18 @@
 // arguments and launch it.
 //
 // Every kernel here streams HBM: nothing is a contraction, so there is no
-// MFMA.  The design points are 16-byte vector loads and stores (8 16-bit
-// values per lane per access), grid-stride loops over 64-bit indices, one
-// read and one write of each fp32 state array per step, and a deterministic
-// two-level (wave shuffle, then LDS) fp64 reduction for the norm whose tree
-// depends only on the element count.
+// MFMA.  Design points, chosen by measurement on MI355X:
+//   * one contiguous tile per block (no grid-stride loop): the set of active
+//     addresses is one window sliding through memory, which keeps all HBM
+//     channels evenly loaded (power-of-two grid strides measured 10-20% slower);
+//   * 4 elements per lane per access, so each wave-wide load or store covers a
+//     contiguous span (8-byte accesses for 16-bit data, 16-byte for fp32);
+//   * all loads of a lane's tile issued before its stores;
+//   * non-temporal loads and stores: nothing is reused, so the caches are
+//     bypassed;
+//   * each fp32 state array is read once and written once per step;
+//   * a deterministic two-level (wave shuffle, then LDS) fp64 reduction whose
+//     tree depends only on the element count.
 //
 //   reduce_kernel   a1: Nd contributions -> rank-order fp32 mean -> 16-bit,
 //                   fused per-block fp64 sums of squares and the inf/NaN flag
@@ -23,6 +30,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -35,6 +43,20 @@
 
 namespace zf {
 namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
 
 // ---------------------------------------------------------------------------
 // 16-bit <-> fp32
@@ -78,21 +100,19 @@ __device__ __forceinline__ bool finite16(uint32_t b) {
     return (b & e) != e;
 }
 
-__device__ __forceinline__ void unpack8(const uint4& w, uint32_t (&h)[8]) {
-    h[0] = w.x & 0xffffu; h[1] = w.x >> 16;
-    h[2] = w.y & 0xffffu; h[3] = w.y >> 16;
-    h[4] = w.z & 0xffffu; h[5] = w.z >> 16;
-    h[6] = w.w & 0xffffu; h[7] = w.w >> 16;
+// Four 16-bit values packed in a u2 (little-endian order).
+__device__ __forceinline__ uint32_t half_of(const u2& w, int k) {
+    const uint32_t word = (k < 2) ? w.x : w.y;
+    return (k & 1) ? (word >> 16) : (word & 0xffffu);
 }
 
-__device__ __forceinline__ uint4 pack8(const uint32_t (&h)[8]) {
-    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                      h[6] | (h[7] << 16));
+__device__ __forceinline__ u2 pack4(const uint32_t (&h)[4]) {
+    return u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
 // ---------------------------------------------------------------------------
 // Deterministic block reduction: xor-butterfly inside each 64-lane wave, then
-// wave 0 adds the per-wave sums in wave order.  Same tree on every run.
+// thread 0 adds the per-wave sums in wave order.  Same tree on every run.
 // ---------------------------------------------------------------------------
 
 template <int BLOCK>
@@ -111,34 +131,42 @@ __device__ __forceinline__ double block_sum(double v) {
 }
 
 // ---------------------------------------------------------------------------
-// a1: reduce
+// Index spaces
 // ---------------------------------------------------------------------------
+
+// With `vec` set, elements [head, head + 4*nq) form the quad body (every
+// pointer aligned for quad accesses there) and the `head` elements before and
+// the tail after it (fewer than 8 in all) are done one by one by the last
+// block.  Without it every element is done one by one, block b taking a
+// contiguous range of elements.
+struct Span {
+    int64_t n;
+    int64_t head;
+    int64_t nq;
+    int vec;
+};
 
 struct Ptrs64 {
     const uint16_t* p[64];
 };
 
-// Elements [head, head + 8*nvec) go through the 16-byte vector body; the
-// `head` elements before and the tail after it through the scalar loop.
-struct Span {
-    int64_t n;
-    int64_t head;
-    int64_t nvec;
-};
+// ---------------------------------------------------------------------------
+// a1: reduce
+// ---------------------------------------------------------------------------
 
 // ND > 0: rank count known at compile time (<= 64), pointers in kernel args.
 // ND == 0: runtime rank count <= 64, pointers in kernel args.
 // ND < 0: runtime rank count > 64, pointers in a device table (workspace).
+// Block b covers quads [b*kPartialQuads, (b+1)*kPartialQuads) of the body (or
+// elements [b*kPartialElems, ...) without `vec`) and writes partials[b].
 template <int DT, int ND>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(Ptrs64 tab, const uint16_t* const* dtab,
+__global__ __launch_bounds__(kReduceBlock) void reduce_kernel(Ptrs64 tab, const uint16_t* const* dtab,
                                                         int nd, Span sp, float inv_nd, float nd_f,
                                                         int pow2, float inv_s,
                                                         uint16_t* __restrict__ out,
                                                         double* __restrict__ partials,
                                                         int32_t* __restrict__ flag) {
 #pragma clang fp contract(off)
-    const int64_t tid = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    const int64_t stride = int64_t(gridDim.x) * kBlock;
     const int ranks = ND > 0 ? ND : nd;
     double sq = 0.0;
     int bad = 0;
@@ -155,44 +183,95 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(Ptrs64 tab, const uint16
         sq += d * d;
         return o;
     };
-
-    for (int64_t i = tid; i < sp.nvec; i += stride) {
-        const int64_t e = sp.head + i * 8;
-        float acc[8];
-        uint32_t h[8];
-        unpack8(*reinterpret_cast<const uint4*>(src(0) + e), h);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = widen<DT>(h[k]);
-        if constexpr (ND > 0) {
-#pragma unroll
-            for (int r = 1; r < ND; ++r) {
-                unpack8(*reinterpret_cast<const uint4*>(src(r) + e), h);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + widen<DT>(h[k]);
-            }
-        } else {
-            for (int r = 1; r < ranks; ++r) {
-                unpack8(*reinterpret_cast<const uint4*>(src(r) + e), h);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + widen<DT>(h[k]);
-            }
-        }
-        uint32_t o[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = finish(acc[k]);
-        *reinterpret_cast<uint4*>(out + e) = pack8(o);
-    }
-
-    const int64_t tail0 = sp.head + 8 * sp.nvec;
-    const int64_t nscalar = sp.head + (sp.n - tail0);
-    for (int64_t k = tid; k < nscalar; k += stride) {
-        const int64_t e = k < sp.head ? k : tail0 + (k - sp.head);
+    auto quad_src = [&](int r) { return reinterpret_cast<const u2*>(src(r) + sp.head); };
+    u2* qout = reinterpret_cast<u2*>(out + sp.head);
+    auto one_element = [&](int64_t e) {
         float acc = widen<DT>(src(0)[e]);
         for (int r = 1; r < ranks; ++r) acc = acc + widen<DT>(src(r)[e]);
         out[e] = static_cast<uint16_t>(finish(acc));
+    };
+
+    if (sp.vec) {
+        const int64_t q0 = int64_t(blockIdx.x) * kPartialQuads + threadIdx.x;
+        for (int t = 0; t < kPartialTiles; ++t) {
+            const int64_t tq = q0 + int64_t(t) * kReduceTileQuads;
+            if (tq - threadIdx.x + kReduceTileQuads <= sp.nq) {
+                // Full tile: this lane's kReduceQuadsPerLane quads, loads before math.
+                float acc[kReduceQuadsPerLane][4];
+#pragma unroll
+                for (int u = 0; u < kReduceQuadsPerLane; ++u) {
+                    const u2 w = ld_stream(quad_src(0) + tq + u * kReduceBlock);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) acc[u][k] = widen<DT>(half_of(w, k));
+                }
+                if constexpr (ND > 0) {
+                    // Up to 16 ranks unroll fully; beyond, 8 ranks' loads are in
+                    // flight at a time (a full unroll spills registers).  The
+                    // summation order is rank order either way.
+                    constexpr int kRankUnroll = ND > 16 ? 8 : ND;
+#pragma unroll kRankUnroll
+                    for (int r = 1; r < ND; ++r) {
+                        u2 w[kReduceQuadsPerLane];
+#pragma unroll
+                        for (int u = 0; u < kReduceQuadsPerLane; ++u) w[u] = ld_stream(quad_src(r) + tq + u * kReduceBlock);
+#pragma unroll
+                        for (int u = 0; u < kReduceQuadsPerLane; ++u)
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) acc[u][k] = acc[u][k] + widen<DT>(half_of(w[u], k));
+                    }
+                } else {
+                    for (int r = 1; r < ranks; ++r) {
+                        u2 w[kReduceQuadsPerLane];
+#pragma unroll
+                        for (int u = 0; u < kReduceQuadsPerLane; ++u) w[u] = ld_stream(quad_src(r) + tq + u * kReduceBlock);
+#pragma unroll
+                        for (int u = 0; u < kReduceQuadsPerLane; ++u)
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) acc[u][k] = acc[u][k] + widen<DT>(half_of(w[u], k));
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kReduceQuadsPerLane; ++u) {
+                    uint32_t o[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = finish(acc[u][k]);
+                    st_stream(qout + tq + u * kReduceBlock, pack4(o));
+                }
+            } else {
+                // Last, partial tile of the body.
+                for (int u = 0; u < kReduceQuadsPerLane; ++u) {
+                    const int64_t q = tq + u * kReduceBlock;
+                    if (q >= sp.nq) break;
+                    float acc[4];
+                    u2 w = quad_src(0)[q];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) acc[k] = widen<DT>(half_of(w, k));
+                    for (int r = 1; r < ranks; ++r) {
+                        w = quad_src(r)[q];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) acc[k] = acc[k] + widen<DT>(half_of(w, k));
+                    }
+                    uint32_t o[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = finish(acc[k]);
+                    qout[q] = pack4(o);
+                }
+                break;
+            }
+        }
+        if (blockIdx.x == gridDim.x - 1) {
+            const int64_t tail0 = sp.head + 4 * sp.nq;
+            const int64_t nscalar = sp.head + (sp.n - tail0);
+            for (int64_t k = threadIdx.x; k < nscalar; k += kReduceBlock)
+                one_element(k < sp.head ? k : tail0 + (k - sp.head));
+        }
+    } else {
+        const int64_t e0 = int64_t(blockIdx.x) * kPartialElems;
+        const int64_t e1 = e0 + kPartialElems < sp.n ? e0 + kPartialElems : sp.n;
+        for (int64_t e = e0 + threadIdx.x; e < e1; e += kReduceBlock) one_element(e);
     }
 
-    const double total = block_sum<kBlock>(sq);
+    const double total = block_sum<kReduceBlock>(sq);
     const int any_bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) {
         partials[blockIdx.x] = total;
@@ -205,11 +284,9 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(Ptrs64 tab, const uint16
 // ---------------------------------------------------------------------------
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void sumsq_kernel(const uint16_t* __restrict__ g, Span sp,
+__global__ __launch_bounds__(kReduceBlock) void sumsq_kernel(const uint16_t* __restrict__ g, Span sp,
                                                        float inv_s, double* __restrict__ partials,
                                                        int32_t* __restrict__ flag) {
-    const int64_t tid = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    const int64_t stride = int64_t(gridDim.x) * kBlock;
     double sq = 0.0;
     int bad = 0;
     auto add = [&](uint32_t b) {
@@ -217,17 +294,42 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(const uint16_t* __restric
         const double d = double(widen<DT>(b)) * double(inv_s);
         sq += d * d;
     };
-    for (int64_t i = tid; i < sp.nvec; i += stride) {
-        uint32_t h[8];
-        unpack8(*reinterpret_cast<const uint4*>(g + sp.head + i * 8), h);
+    const u2* qg = reinterpret_cast<const u2*>(g + sp.head);
+    if (sp.vec) {
+        const int64_t q0 = int64_t(blockIdx.x) * kPartialQuads + threadIdx.x;
+        for (int t = 0; t < kPartialTiles; ++t) {
+            const int64_t tq = q0 + int64_t(t) * kReduceTileQuads;
+            if (tq - threadIdx.x + kReduceTileQuads <= sp.nq) {
+                u2 w[kReduceQuadsPerLane];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) add(h[k]);
+                for (int u = 0; u < kReduceQuadsPerLane; ++u) w[u] = ld_stream(qg + tq + u * kReduceBlock);
+#pragma unroll
+                for (int u = 0; u < kReduceQuadsPerLane; ++u)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) add(half_of(w[u], k));
+            } else {
+                for (int u = 0; u < kReduceQuadsPerLane; ++u) {
+                    const int64_t q = tq + u * kReduceBlock;
+                    if (q >= sp.nq) break;
+                    const u2 w = qg[q];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) add(half_of(w, k));
+                }
+                break;
+            }
+        }
+        if (blockIdx.x == gridDim.x - 1) {
+            const int64_t tail0 = sp.head + 4 * sp.nq;
+            const int64_t nscalar = sp.head + (sp.n - tail0);
+            for (int64_t k = threadIdx.x; k < nscalar; k += kReduceBlock) add(g[k < sp.head ? k : tail0 + (k - sp.head)]);
+        }
+    } else {
+        const int64_t e0 = int64_t(blockIdx.x) * kPartialElems;
+        const int64_t e1 = e0 + kPartialElems < sp.n ? e0 + kPartialElems : sp.n;
+        for (int64_t e = e0 + threadIdx.x; e < e1; e += kReduceBlock) add(g[e]);
     }
-    const int64_t tail0 = sp.head + 8 * sp.nvec;
-    const int64_t nscalar = sp.head + (sp.n - tail0);
-    for (int64_t k = tid; k < nscalar; k += stride) add(g[k < sp.head ? k : tail0 + (k - sp.head)]);
 
-    const double total = block_sum<kBlock>(sq);
+    const double total = block_sum<kReduceBlock>(sq);
     const int any_bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) {
         partials[blockIdx.x] = total;
@@ -236,14 +338,47 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(const uint16_t* __restric
 }
 
 constexpr int kFinalizeBlock = 1024;
+constexpr int kStageBlock = 256;
+// Up to this many partial sums the finalize reads them directly; above it a
+// first stage folds contiguous chunks into at most kLevel2Max sums.
+constexpr int64_t kSingleStageMax = 8192;
+constexpr int64_t kStageChunkMin = 4096;
 
+// Sums x[lo..hi) with thread t taking x[lo + t], x[lo + t + B], ... into
+// eight accumulators (its j-th value into accumulator j mod 8, eight loads in
+// flight), combined in a fixed order.  The result is the same on every run.
+template <int B>
+__device__ __forceinline__ double thread_sum(const double* __restrict__ x, int64_t lo, int64_t hi) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t k = lo + threadIdx.x;
+    for (; k + 7 * B < hi; k += 8 * B) {
+        double v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = x[k + i * B];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    for (int i = 0; k < hi; k += B, ++i) acc[i] += x[k];
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// First stage: block b folds partials [b*chunk, min((b+1)*chunk, count)).
+__global__ __launch_bounds__(kStageBlock) void fold_kernel(const double* __restrict__ partials,
+                                                           int64_t count, int64_t chunk,
+                                                           double* __restrict__ level2) {
+    const int64_t lo = int64_t(blockIdx.x) * chunk;
+    const int64_t hi = lo + chunk < count ? lo + chunk : count;
+    const double total = block_sum<kStageBlock>(thread_sum<kStageBlock>(partials, lo, hi));
+    if (threadIdx.x == 0) level2[blockIdx.x] = total;
+}
+
+// Sum of `count` values, plus extra[0..n_extra) in order -> norm, clip
+// multiplier, and the non-finite flag.
 __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(
-    const double* __restrict__ partials, int64_t count, const double* __restrict__ extra,
+    const double* __restrict__ values, int64_t count, const double* __restrict__ extra,
     int n_extra, float max_norm, int32_t* __restrict__ flag, double* __restrict__ norm_out,
     float* __restrict__ coef_out) {
-    double s = 0.0;
-    for (int64_t k = threadIdx.x; k < count; k += kFinalizeBlock) s += partials[k];
-    double total = block_sum<kFinalizeBlock>(s);
+    double total = block_sum<kFinalizeBlock>(thread_sum<kFinalizeBlock>(values, 0, count));
     if (threadIdx.x == 0) {
         for (int j = 0; j < n_extra; ++j) total += extra[j];
         const double norm = sqrt(total);
@@ -263,10 +398,10 @@ struct AdamConsts {
     float lr, b1, b2, omb1, omb2, eps, wd, inv_s, inv_bc1, inv_bc2;
 };
 
-// Elements [head, head + 8*nvec) use 16-byte accesses for the 16-bit arrays
-// and two 16-byte accesses per fp32 array.
+// Block b covers quads [b*kAdamTileQuads, (b+1)*kAdamTileQuads) of the body (or
+// elements [b*kAdamTileElems, ...) without `vec`).
 template <int GDT, int PDT>
-__global__ __launch_bounds__(kBlock) void adam_kernel(float* __restrict__ master,
+__global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ master,
                                                       float* __restrict__ m,
                                                       float* __restrict__ v,
                                                       const uint16_t* __restrict__ grad, Span sp,
@@ -276,8 +411,6 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(float* __restrict__ master
                                                       uint16_t* __restrict__ param) {
     if (*flag != 0) return;  // a skipped step writes nothing
     const float gs = c.inv_s * *coef_dev;
-    const int64_t tid = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    const int64_t stride = int64_t(gridDim.x) * kBlock;
 
     auto update = [&](float& p, float& mm, float& vv, uint32_t gb) -> uint32_t {
         const float g = widen<GDT>(gb) * gs;
@@ -287,44 +420,74 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(float* __restrict__ master
         p = p - c.lr * ((mm * c.inv_bc1) / denom + c.wd * p);
         return narrow<PDT>(p);
     };
-
-    for (int64_t i = tid; i < sp.nvec; i += stride) {
-        const int64_t e = sp.head + i * 8;
-        uint32_t h[8];
-        unpack8(*reinterpret_cast<const uint4*>(grad + e), h);
-        float4 p0 = *reinterpret_cast<const float4*>(master + e);
-        float4 p1 = *reinterpret_cast<const float4*>(master + e + 4);
-        float4 m0 = *reinterpret_cast<const float4*>(m + e);
-        float4 m1 = *reinterpret_cast<const float4*>(m + e + 4);
-        float4 v0 = *reinterpret_cast<const float4*>(v + e);
-        float4 v1 = *reinterpret_cast<const float4*>(v + e + 4);
-        uint32_t o[8];
-        o[0] = update(p0.x, m0.x, v0.x, h[0]);
-        o[1] = update(p0.y, m0.y, v0.y, h[1]);
-        o[2] = update(p0.z, m0.z, v0.z, h[2]);
-        o[3] = update(p0.w, m0.w, v0.w, h[3]);
-        o[4] = update(p1.x, m1.x, v1.x, h[4]);
-        o[5] = update(p1.y, m1.y, v1.y, h[5]);
-        o[6] = update(p1.z, m1.z, v1.z, h[6]);
-        o[7] = update(p1.w, m1.w, v1.w, h[7]);
-        *reinterpret_cast<float4*>(master + e) = p0;
-        *reinterpret_cast<float4*>(master + e + 4) = p1;
-        *reinterpret_cast<float4*>(m + e) = m0;
-        *reinterpret_cast<float4*>(m + e + 4) = m1;
-        *reinterpret_cast<float4*>(v + e) = v0;
-        *reinterpret_cast<float4*>(v + e + 4) = v1;
-        *reinterpret_cast<uint4*>(param + e) = pack8(o);
-    }
-    const int64_t tail0 = sp.head + 8 * sp.nvec;
-    const int64_t nscalar = sp.head + (sp.n - tail0);
-    for (int64_t k = tid; k < nscalar; k += stride) {
-        const int64_t e = k < sp.head ? k : tail0 + (k - sp.head);
+    auto update4 = [&](f4& p, f4& mm, f4& vv, const u2& g) -> u2 {
+        float pp[4] = {p.x, p.y, p.z, p.w}, ma[4] = {mm.x, mm.y, mm.z, mm.w}, va[4] = {vv.x, vv.y, vv.z, vv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = update(pp[k], ma[k], va[k], half_of(g, k));
+        p = f4{pp[0], pp[1], pp[2], pp[3]};
+        mm = f4{ma[0], ma[1], ma[2], ma[3]};
+        vv = f4{va[0], va[1], va[2], va[3]};
+        return pack4(o);
+    };
+    auto one_element = [&](int64_t e) {
         float p = master[e], mm = m[e], vv = v[e];
         const uint32_t o = update(p, mm, vv, grad[e]);
         master[e] = p;
         m[e] = mm;
         v[e] = vv;
         param[e] = static_cast<uint16_t>(o);
+    };
+
+    if (sp.vec) {
+        f4* qp = reinterpret_cast<f4*>(master + sp.head);
+        f4* qm = reinterpret_cast<f4*>(m + sp.head);
+        f4* qv = reinterpret_cast<f4*>(v + sp.head);
+        const u2* qg = reinterpret_cast<const u2*>(grad + sp.head);
+        u2* qo = reinterpret_cast<u2*>(param + sp.head);
+        const int64_t tq = int64_t(blockIdx.x) * kAdamTileQuads + threadIdx.x;
+        if (tq - threadIdx.x + kAdamTileQuads <= sp.nq) {
+            u2 g[kAdamQuadsPerLane];
+            f4 p[kAdamQuadsPerLane], mm[kAdamQuadsPerLane], vv[kAdamQuadsPerLane];
+#pragma unroll
+            for (int u = 0; u < kAdamQuadsPerLane; ++u) {
+                const int64_t q = tq + u * kAdamBlock;
+                g[u] = ld_stream(qg + q);
+                p[u] = ld_stream(qp + q);
+                mm[u] = ld_stream(qm + q);
+                vv[u] = ld_stream(qv + q);
+            }
+#pragma unroll
+            for (int u = 0; u < kAdamQuadsPerLane; ++u) {
+                const int64_t q = tq + u * kAdamBlock;
+                const u2 o = update4(p[u], mm[u], vv[u], g[u]);
+                st_stream(qp + q, p[u]);
+                st_stream(qm + q, mm[u]);
+                st_stream(qv + q, vv[u]);
+                st_stream(qo + q, o);
+            }
+        } else {
+            for (int u = 0; u < kAdamQuadsPerLane; ++u) {
+                const int64_t q = tq + u * kAdamBlock;
+                if (q >= sp.nq) break;
+                f4 p = qp[q], mm = qm[q], vv = qv[q];
+                const u2 o = update4(p, mm, vv, qg[q]);
+                qp[q] = p;
+                qm[q] = mm;
+                qv[q] = vv;
+                qo[q] = o;
+            }
+        }
+        if (blockIdx.x == gridDim.x - 1) {
+            const int64_t tail0 = sp.head + 4 * sp.nq;
+            const int64_t nscalar = sp.head + (sp.n - tail0);
+            for (int64_t k = threadIdx.x; k < nscalar; k += kAdamBlock)
+                one_element(k < sp.head ? k : tail0 + (k - sp.head));
+        }
+    } else {
+        const int64_t e0 = int64_t(blockIdx.x) * kAdamTileElems;
+        const int64_t e1 = e0 + kAdamTileElems < sp.n ? e0 + kAdamTileElems : sp.n;
+        for (int64_t e = e0 + threadIdx.x; e < e1; e += kAdamBlock) one_element(e);
     }
 }
 
@@ -332,10 +495,16 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(float* __restrict__ master
 // a4: gather one unit
 // ---------------------------------------------------------------------------
 
-// Block (x, r) copies part of owner r's slice of one unit.  `vec` selects
-// 16-byte copies (everything aligned) or 2-byte copies.
+constexpr int kGatherBlock = 512;
+constexpr int kGatherOctsPerLane = 2;                                     // 16-byte pieces
+constexpr int64_t kGatherTileOcts = int64_t(kGatherBlock) * kGatherOctsPerLane;
+constexpr int64_t kGatherTileElems = 8 * kGatherTileOcts;
+
+// Block (x, r) copies tile x of owner r's slice of one unit.  `vec` selects
+// 16-byte pieces (everything 16-byte aligned, slice a multiple of 8) or
+// element-by-element copies.
 template <bool DEVICE_TABLE>
-__global__ __launch_bounds__(kBlock) void gather_kernel(Ptrs64 tab, const uint16_t* const* dtab,
+__global__ __launch_bounds__(kGatherBlock) void gather_kernel(Ptrs64 tab, const uint16_t* const* dtab,
                                                         int64_t slice, int64_t shard_base,
                                                         int64_t full_base, int vec,
                                                         uint16_t* __restrict__ full) {
@@ -345,15 +514,27 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(Ptrs64 tab, const uint16
     else src = tab.p[r];
     src += shard_base;
     uint16_t* dst = full + full_base + int64_t(r) * slice;
-    const int64_t tid = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    const int64_t stride = int64_t(gridDim.x) * kBlock;
     if (vec) {
+        const u4* s4 = reinterpret_cast<const u4*>(src);
+        u4* d4 = reinterpret_cast<u4*>(dst);
         const int64_t nv = slice / 8;
-        const uint4* s4 = reinterpret_cast<const uint4*>(src);
-        uint4* d4 = reinterpret_cast<uint4*>(dst);
-        for (int64_t i = tid; i < nv; i += stride) d4[i] = s4[i];
+        const int64_t t0 = int64_t(blockIdx.x) * kGatherTileOcts + threadIdx.x;
+        if (t0 - threadIdx.x + kGatherTileOcts <= nv) {
+            u4 x[kGatherOctsPerLane];
+#pragma unroll
+            for (int u = 0; u < kGatherOctsPerLane; ++u) x[u] = ld_stream(s4 + t0 + u * kGatherBlock);
+#pragma unroll
+            for (int u = 0; u < kGatherOctsPerLane; ++u) st_stream(d4 + t0 + u * kGatherBlock, x[u]);
+        } else {
+            for (int u = 0; u < kGatherOctsPerLane; ++u) {
+                const int64_t i = t0 + u * kGatherBlock;
+                if (i < nv) d4[i] = s4[i];
+            }
+        }
     } else {
-        for (int64_t i = tid; i < slice; i += stride) dst[i] = src[i];
+        const int64_t e0 = int64_t(blockIdx.x) * kGatherTileElems;
+        const int64_t e1 = e0 + kGatherTileElems < slice ? e0 + kGatherTileElems : slice;
+        for (int64_t e = e0 + threadIdx.x; e < e1; e += kGatherBlock) dst[e] = src[e];
     }
 }
 
@@ -377,38 +558,34 @@ bool pow2_positive(float x) {
     return std::frexp(x, &e) == 0.5f;
 }
 
-// Vector span for a set of arrays: `head` scalar elements bring every pointer
-// to a 16-byte boundary; if no common head exists everything is scalar.
+// Quad span for a set of arrays: `head` elements (0..3) bring every 16-bit
+// pointer to an 8-byte and every fp32 pointer to a 16-byte boundary.  If no
+// common head exists (or n is tiny) every element goes one by one.
 Span make_span(int64_t n, const void* const* ptrs16, int n16, const void* const* ptrs32, int n32) {
-    Span sp{n, n, 0};
+    Span sp{n, 0, 0, 0};
     if (n == 0) return sp;
-    const void* lead = n16 > 0 ? ptrs16[0] : ptrs32[0];
     int64_t head;
     if (n16 > 0) {
-        const uintptr_t mis = addr(lead) & 15;
+        const uintptr_t mis = addr(ptrs16[0]) & 7;
         if (mis & 1) return sp;
-        head = int64_t((16 - mis) & 15) / 2;
+        head = int64_t((8 - mis) & 7) / 2;
     } else {
-        const uintptr_t mis = addr(lead) & 15;
+        const uintptr_t mis = addr(ptrs32[0]) & 15;
         if (mis & 3) return sp;
         head = int64_t((16 - mis) & 15) / 4;
     }
     for (int i = 0; i < n16; ++i)
-        if (((addr(ptrs16[i]) + 2 * uintptr_t(head)) & 15) != 0) return sp;
+        if (((addr(ptrs16[i]) + 2 * uintptr_t(head)) & 7) != 0) return sp;
     for (int i = 0; i < n32; ++i)
         if (((addr(ptrs32[i]) + 4 * uintptr_t(head)) & 15) != 0) return sp;
-    if (head >= n) return sp;
+    if (head + 4 > n) return sp;
     sp.head = head;
-    sp.nvec = (n - head) / 8;
+    sp.nq = (n - head) / 4;
+    sp.vec = 1;
     return sp;
 }
 
-unsigned grid_for(int64_t work_items, int64_t max_blocks) {
-    int64_t b = (work_items + kBlock - 1) / kBlock;
-    if (b < 1) b = 1;
-    if (b > max_blocks) b = max_blocks;
-    return unsigned(b);
-}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int hip_status(hipError_t e, const char* where) {
     if (e != hipSuccess) return fail(ZERO_EHIP, std::string(where) + ": " + hipGetErrorString(e));
@@ -435,7 +612,7 @@ hipError_t launch_reduce(int nd, dim3 grid, hipStream_t s, const Ptrs64& tab,
                          const uint16_t* const* dtab, Span sp, float inv_nd, float nd_f, int pow2,
                          float inv_s, uint16_t* out, double* partials, int32_t* flag) {
 #define ZF_REDUCE(ND_)                                                                             \
-    return launch(reduce_kernel<DT, ND_>, grid, dim3(kBlock), s, tab, dtab, nd, sp, inv_nd, nd_f, \
+    return launch(reduce_kernel<DT, ND_>, grid, dim3(kReduceBlock), s, tab, dtab, nd, sp, inv_nd, nd_f, \
                   pow2, inv_s, out, partials, flag)
     switch (dtab ? -1 : nd) {
         case -1: ZF_REDUCE(-1);
@@ -456,14 +633,11 @@ hipError_t launch_adam(int pdt, dim3 grid, hipStream_t s, float* master, float* 
                        const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
                        const int32_t* flag, uint16_t* param) {
     if (pdt == ZERO_F16)
-        return launch(adam_kernel<GDT, ZERO_F16>, grid, dim3(kBlock), s, master, m, v, grad, sp, c,
+        return launch(adam_kernel<GDT, ZERO_F16>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c,
                       coef, flag, param);
-    return launch(adam_kernel<GDT, ZERO_BF16>, grid, dim3(kBlock), s, master, m, v, grad, sp, c, coef,
+    return launch(adam_kernel<GDT, ZERO_BF16>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c, coef,
                   flag, param);
 }
-
-constexpr int64_t kMaxAdamBlocks = 2048;
-constexpr int64_t kMaxGatherBlocksX = 1024;
 
 }  // namespace
 }  // namespace zf
@@ -508,7 +682,7 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t blocks = partial_blocks(n);
-    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kTableBytes) + int64_t(set) * blocks;
+    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kPartialsOffset) + int64_t(set) * blocks;
     Ptrs64 tab{};
     const uint16_t* const* dtab = nullptr;
     std::vector<const void*> ptrs(nd, nullptr);
@@ -526,7 +700,7 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
     }
     std::vector<const void*> all16(ptrs);
     all16.push_back(reduced_out);
-    const Span sp = n > 0 ? make_span(n, all16.data(), int(all16.size()), nullptr, 0) : Span{0, 0, 0};
+    const Span sp = make_span(n, all16.data(), int(all16.size()), nullptr, 0);
     int e2;
     const bool pow2 = std::frexp(double(nd), &e2) == 0.5;
     const float inv_nd = pow2 ? 1.0f / float(nd) : 0.0f;
@@ -570,23 +744,36 @@ int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t blocks = partial_blocks(n);
-    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kTableBytes);
+    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kPartialsOffset);
+    double* level2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + kTableBytes);
     if (grad != nullptr && n > 0) {
         const void* p16[1] = {grad};
-        const Span sp = n > 0 ? make_span(n, p16, 1, nullptr, 0) : Span{0, 0, 0};
+        const Span sp = make_span(n, p16, 1, nullptr, 0);
         const uint16_t* g16 = static_cast<const uint16_t*>(grad);
         const hipError_t e =
             dtype == ZERO_F16
-                ? launch(sumsq_kernel<ZERO_F16>, dim3(unsigned(blocks)), dim3(kBlock), s, g16, sp,
+                ? launch(sumsq_kernel<ZERO_F16>, dim3(unsigned(blocks)), dim3(kReduceBlock), s, g16, sp,
                          inv_loss_scale, partials, flag)
-                : launch(sumsq_kernel<ZERO_BF16>, dim3(unsigned(blocks)), dim3(kBlock), s, g16, sp,
+                : launch(sumsq_kernel<ZERO_BF16>, dim3(unsigned(blocks)), dim3(kReduceBlock), s, g16, sp,
                          inv_loss_scale, partials, flag);
         if (e != hipSuccess) return hip_status(e, fn);
     }
     // With n = 0 every partial sum is zero by definition: none is read, so an
     // empty gradient needs no partials pass and no earlier launch.
     const int64_t count = n > 0 ? int64_t(n_sets) * blocks : 0;
-    return hip_status(launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), s, partials, count,
+    const double* values = partials;
+    int64_t n_values = count;
+    if (count > kSingleStageMax) {
+        const int64_t groups = std::min<int64_t>(kLevel2Max, ceil_div(count, kStageChunkMin));
+        const int64_t chunk = ceil_div(count, groups);
+        const int64_t used = ceil_div(count, chunk);
+        const hipError_t e = launch(fold_kernel, dim3(unsigned(used)), dim3(kStageBlock), s, partials, count,
+                                    chunk, level2);
+        if (e != hipSuccess) return hip_status(e, fn);
+        values = level2;
+        n_values = used;
+    }
+    return hip_status(launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), s, values, n_values,
                              extra_sumsq, n_extra, max_norm, flag, norm_out, coef_out),
                       fn);
 }
@@ -646,7 +833,8 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
     const void* p32[3] = {master, m, v};
     const Span sp = make_span(n, p16, 2, p32, 3);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid(grid_for(sp.nvec > 0 ? sp.nvec : n, kMaxAdamBlocks));
+    const int64_t blocks = sp.vec ? std::max<int64_t>(1, ceil_div(sp.nq, kAdamTileQuads)) : ceil_div(n, kAdamTileElems);
+    const dim3 grid{unsigned(blocks)};
     const uint16_t* g16 = static_cast<const uint16_t*>(grad);
     uint16_t* p16o = static_cast<uint16_t*>(param_out);
     const hipError_t e =
@@ -699,13 +887,13 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
         const UnitInfo& ui = plan->units[u];
         if (ui.slice_numel == 0) continue;
         const int vec = aligned ? 1 : 0;
-        const int64_t items = vec ? ui.slice_numel / 8 : ui.slice_numel;
-        const dim3 grid(grid_for(items, kMaxGatherBlocksX), unsigned(owners));
+        const int64_t bx = vec ? ceil_div(ui.slice_numel / 8, kGatherTileOcts) : ceil_div(ui.slice_numel, kGatherTileElems);
+        const dim3 grid(unsigned(std::max<int64_t>(bx, 1)), unsigned(owners));
         uint16_t* f16 = static_cast<uint16_t*>(full);
         const hipError_t e =
-            device_table ? launch(gather_kernel<true>, grid, dim3(kBlock), s, tab, dtab, ui.slice_numel,
+            device_table ? launch(gather_kernel<true>, grid, dim3(kGatherBlock), s, tab, dtab, ui.slice_numel,
                                   ui.shard_base, ui.full_base, vec, f16)
-                         : launch(gather_kernel<false>, grid, dim3(kBlock), s, tab, dtab, ui.slice_numel,
+                         : launch(gather_kernel<false>, grid, dim3(kGatherBlock), s, tab, dtab, ui.slice_numel,
                                   ui.shard_base, ui.full_base, vec, f16);
         if (e != hipSuccess) return hip_status(e, fn);
     }

@@ -30,12 +30,8 @@ int ok() {
 }
 
 int64_t partial_blocks(int64_t n) {
-    // One block per 256 16-byte vectors, at least 1, at most kMaxPartialBlocks.
-    int64_t vecs = (n + 7) / 8;
-    int64_t b = (vecs + kBlock - 1) / kBlock;
-    if (b < 1) b = 1;
-    if (b > kMaxPartialBlocks) b = kMaxPartialBlocks;
-    return b;
+    const int64_t b = (n + kPartialElems - 1) / kPartialElems;
+    return b < 1 ? 1 : b;
 }
 
 }  // namespace zf
@@ -219,7 +215,7 @@ int64_t zero_workspace_bytes(int64_t n, int n_sets) {
         return -1;
     }
     zf::ok();
-    return zf::kTableBytes + int64_t(n_sets) * zf::partial_blocks(n) * int64_t(sizeof(double));
+    return zf::kPartialsOffset + int64_t(n_sets) * zf::partial_blocks(n) * int64_t(sizeof(double));
 }
 
 }  // extern "C"
