@@ -26,7 +26,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flat_amd", "csrc", "kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "zero_sharded_mixed_flat_amd", "csrc", f)
+                  for f in ("kernels.hip", "internal.h")]
+COPY_ELEMS = 1 << 31            # the reference copy: 4 GiB of 16-bit values
+COPY_BYTES_EACH_WAY = 2 * COPY_ELEMS
 
 
 def _log(msg):
@@ -34,8 +37,11 @@ def _log(msg):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
@@ -108,6 +114,73 @@ def cpu_baseline(run, budget_s=12.0):
     }, parity
 
 
+def _short(name):
+    name = name.replace("zf::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    return name.replace("void ", "").split("(")[0]
+
+
+def summarize_trace(stats_csv, command):
+    """Markdown table of a rocprofv3 --stats kernel summary (kernels of this library first)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    ours = [r for r in rows if "zf::" in r["Name"]]
+    other = [r for r in rows if "zf::" not in r["Name"]]
+    out = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in ours + other[:4]:
+        out.append(f"| `{_short(r['Name'])[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    return "\n".join(out) + "\n"
+
+
+def summarize_counters(fetch_csv, write_csv, workload, alg_bytes, commands):
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, scaled by the reference copy.
+
+    The reference copy is the 4 GiB -> 4 GiB gather dispatch in the same run;
+    its known byte counts give one scale factor per counter.  Returns the
+    markdown summary and the traffic entry for the dominant (AdamW) kernel.
+    """
+    import csv
+    from collections import defaultdict
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        acc = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter or "zf::" not in r["Kernel_Name"]:
+                continue
+            acc[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        per[counter] = {k: sum(v) / len(v) for k, v in acc.items()}
+    copy_grid = COPY_ELEMS // 8 // 2    # 16-byte pieces, two per lane: one lane per 16 elements
+    copy_key = [k for k in per["FETCH_SIZE"] if k[0].startswith("gather_kernel") and k[1] == copy_grid]
+    if not copy_key:
+        raise RuntimeError("no reference copy dispatch in the counter files")
+    ck = copy_key[0]
+    ref_kib = COPY_BYTES_EACH_WAY / 1024
+    fetch_scale = ref_kib / per["FETCH_SIZE"][ck]
+    write_scale = ref_kib / per["WRITE_SIZE"][ck]
+    out = ["# HBM byte counters", "", "Commands:", "", "```"] + list(commands) + ["```", "",
+           f"Reference: the gather kernel copying {COPY_BYTES_EACH_WAY} bytes to another buffer "
+           f"(grid {ck[1]}) read FETCH_SIZE {per['FETCH_SIZE'][ck]:.6g} KiB and WRITE_SIZE "
+           f"{per['WRITE_SIZE'][ck]:.6g} KiB per dispatch, so the scale factors are "
+           f"{fetch_scale:.5f} (fetch) and {write_scale:.5f} (write).", "",
+           "| kernel | grid | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes read | scaled bytes written | scaled total |",
+           "|---|---|---|---|---|---|---|"]
+    entry = None
+    for k in sorted(per["FETCH_SIZE"], key=lambda k: -per["FETCH_SIZE"][k]):
+        f = per["FETCH_SIZE"][k]
+        w = per["WRITE_SIZE"].get(k, float("nan"))
+        rb, wb = f * 1024 * fetch_scale, w * 1024 * write_scale
+        out.append(f"| `{k[0]}` | {k[1]} | {f:.6g} | {w:.6g} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} |")
+        if k[0].startswith("adam_kernel"):
+            entry = {"kernel": k[0], "bytes_per_launch": rb + wb, "bytes_read": rb, "bytes_written": wb,
+                     "algorithmic_bytes_per_launch": alg_bytes, "fetch_scale": fetch_scale,
+                     "write_scale": write_scale, "kernel_source_sha256_16": kernel_source_hash()}
+    if entry:
+        out += ["", f"AdamW: {entry['bytes_per_launch']:.5g} bytes per launch against "
+                f"{alg_bytes:.5g} algorithmic bytes ({entry['bytes_per_launch'] / alg_bytes:.4f}x)."]
+    return "\n".join(out) + "\n", entry
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +189,37 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV",
+                    help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize FETCH_SIZE / WRITE_SIZE counter files, update profiles/traffic.json")
+    ap.add_argument("--command", action="append", default=[],
+                    help="the command(s) that produced the files being summarized")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, "\n".join(args.command)), end="")
+        return 0
+    if args.summarize_counters:
+        from zero_sharded_mixed_flat_amd import workloads as _wl
+        name = args.workload or _wl.BENCH_DEFAULT
+        w = _wl.get(name)
+        from zero_sharded_mixed_flat_amd import abi as _abi
+        n, _ = _abi.Plan(w.units, w.nd, w.stage, w.align).rank(0)
+        owners = w.nd if w.all_ranks else 1
+        text, entry = summarize_counters(*args.summarize_counters, name, 28 * n * owners, args.command)
+        print(text, end="")
+        if entry:
+            try:
+                with open(TRAFFIC_FILE) as f:
+                    data = json.load(f)
+            except (OSError, ValueError):
+                data = {}
+            data[name] = entry
+            with open(TRAFFIC_FILE, "w") as f:
+                json.dump(data, f, indent=1, sort_keys=True)
+                f.write("\n")
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU; --gpus {args.gpus} is not supported "
@@ -179,6 +282,29 @@ def main():
             acc[p] += ev[p][0].elapsed_time(ev[p][1])
     kern_ms = {p: acc[p] / args.steps for p in phases}
 
+    # Plain-copy ceiling in the same run: the gather kernel on a one-unit,
+    # one-owner plan is a pure copy of 4 GiB into another 4 GiB buffer, with
+    # the same tiled non-temporal accesses as the step's kernels.  It is also
+    # the reference of known size for scaling the HBM byte counters.
+    from zero_sharded_mixed_flat_amd import abi
+    copy_elems = COPY_ELEMS
+    copy_plan = abi.Plan([copy_elems], 1, 3, 8)
+    src = torch.empty(copy_elems, dtype=torch.float16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    abi.zero_gather_params(copy_plan, [src], 0, 1, "f16", dst, run.ws)
+    torch.cuda.synchronize()
+    copy_ms = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        abi.zero_gather_params(copy_plan, [src], 0, 1, "f16", dst, run.ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(a.elapsed_time(b))
+    copy_bytes = 2 * 2 * copy_elems
+    copy_gbs = copy_bytes / (sum(copy_ms) / len(copy_ms) * 1e-3) / 1e9
+    del src, dst
+
     owned = run.n * len(run.owners)
     alg_bytes = run.algorithmic_bytes()
     adam_bytes = 28 * owned
@@ -209,6 +335,10 @@ def main():
         "hbm_frac_of_peak": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": alg_bytes,
         "kernel_ms": {k: round(v, 6) for k, v in kern_ms.items() if v > 0},
+        "copy_ceiling": {"kernel": "gather_kernel as a plain 4 GiB -> 4 GiB copy", "gbs": copy_gbs,
+                         "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+                         "step_frac_of_copy": step_gbs / copy_gbs,
+                         "adam_frac_of_copy": adam_gbs / copy_gbs},
         "roofline": {
             "bound": "hbm",
             "kernel": "adam_kernel",

@@ -230,6 +230,24 @@ def test_norm_two_stage_finalize(abi, n, sets):
         assert np.array_equal(_bits(out), g)                      # nd = 1 is the identity
 
 
+@pytest.mark.parametrize("n, offset", [(20_000_003, 0), (17_000_001, 3), (16_777_216 + 2048 * 3, 1)])
+def test_prereduced_norm_large(abi, n, offset):
+    # The partials pass over one array at sizes with more than 8192 partial
+    # sums (two-stage finalize), aligned and misaligned.
+    _note(f"prereduced norm n={n} offset={offset}")
+    rng = np.random.default_rng(n)
+    g = _rand16(rng, n, 1e-4, "bf16")
+    ws = _ws(abi, n, 1)
+    flag, norm, coef = _scalars()
+    dg = _dev16(g, "bf16", offset=offset)
+    abi.zero_grad_norm(dg, n, "bf16", 1.0, ws, 1, None, 0, 0.5, flag, norm, coef)
+    torch.cuda.synchronize()
+    ref = step.norm_from_sumsq(step.sumsq_exact(g, "bf16"))
+    assert abs(norm.item() - ref) <= 1e-12 * ref
+    assert float(coef.item()) == pytest.approx(float(step.clip_coef(ref, 0.5)), rel=2 ** -22)
+    assert int(flag.item()) == 0
+
+
 # ---------------------------------------------------------------------------
 # a2 standalone partials pass + extra partial sums
 # ---------------------------------------------------------------------------

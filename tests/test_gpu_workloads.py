@@ -1,0 +1,154 @@
+"""GPU parity at the full sizes of the four large workloads, in the launch
+configuration bench.py times (the same step driver and buffers).
+
+The sum of squares of a 1e9-1e10 element gradient is checked through a
+property that holds at any size: every rank's contribution (or the
+pre-reduced gradient) is tiled with a ragged period P, so the reduced
+gradient is tiled too and its exact sum of squares is
+(n // P) * S(one period) + S(first n % P elements).  Everything else
+(reduced gradient bit for bit, master/m/v, 16-bit parameters, gathered
+buffer) is compared on sampled chunks -- first, last, random and unit
+boundaries -- computed one by one by the oracle from the actual device
+inputs copied back before the step.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import partition, rounding, step
+from oracle.step import AdamHparams
+from zero_sharded_mixed_flat_amd import synth, workloads
+
+pytestmark = pytest.mark.gpu
+
+PERIOD = (1 << 20) + 37
+CHUNK = 1 << 16
+
+
+@pytest.fixture
+def runner():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_sharded_mixed_flat_amd import runner as _runner
+    yield _runner
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def _hp(w):
+    return AdamHparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                       inv_loss_scale=w.inv_loss_scale, max_norm=w.max_norm)
+
+
+def _state_ok(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bad = np.flatnonzero(np.abs(got - ref) > 1e-9 + 1e-6 * np.abs(ref))
+    assert bad.size == 0, f"{what}: {bad.size} out of tolerance, e.g. gpu {got[bad[:3]]} oracle {ref[bad[:3]]}"
+
+
+def _ulp_ok(got, ref, what):
+    d = np.abs(rounding.ordered16(got) - rounding.ordered16(ref))
+    assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} params more than 1 ulp apart"
+
+
+def _offsets(n, extra=(), seed=0):
+    rng = np.random.default_rng(seed)
+    offs = {0, max(0, n - CHUNK)}
+    offs.update(int(x) for x in rng.integers(0, max(1, n - CHUNK), size=6))
+    offs.update(min(max(0, int(x)), max(0, n - CHUNK)) for x in extra)
+    return sorted(offs)
+
+
+def _period_sumsq(reduced_period, tail_len, n, dtype, inv_s):
+    """Exact sum of squares of a vector tiled with the given period."""
+    whole = step.sumsq_exact(reduced_period, dtype, inv_s)
+    tail = step.sumsq_exact(reduced_period[:tail_len], dtype, inv_s)
+    return (n // len(reduced_period)) * whole + tail
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_nd8_z2", "gpt2_1p5b_nd16_z1", "paper_7p5b_nd64_z3",
+                                  "gpt3_175b_nd16_z1"])
+def test_full_size_step(runner, name):
+    w = workloads.get(name)
+    _note(f"full-size {name}: allocating")
+    run = runner.RankStep(w, seed=3, tile_period=PERIOD)
+    n = run.n
+    plan = partition.make_plan(w.units, w.nd, w.stage, w.align)
+    assert n == plan.shard_numel
+    hp = _hp(w)
+    unit_edges = [u.shard_base for u in plan.units[1:]] if w.stage == 3 else []
+    offs = _offsets(n, extra=[e - CHUNK // 2 for e in unit_edges[:4]], seed=len(name))
+
+    # Inputs, copied back before the step.
+    def grads_at(lo, hi):
+        if w.pre_reduced:
+            return None, synth.bits(run.grad[lo:hi])
+        return [synth.bits(c[lo:hi]) for c in run.contribs(0)], None
+
+    period_contribs, period_grad = grads_at(0, PERIOD)
+    chunks = {}
+    for o in offs:
+        contribs, grad = grads_at(o, o + CHUNK)
+        state = tuple(t[0, o:o + CHUNK].cpu().numpy() for t in (run.master, run.m, run.v))
+        chunks[o] = (contribs, grad, state)
+    others = None
+    if run.shards is not None:
+        others = {o: [synth.bits(run.shards[r, o:o + CHUNK]) for r in range(w.nd)] for o in offs}
+    torch.cuda.synchronize()
+
+    _note(f"full-size {name}: step over n={n}")
+    run.step()
+    torch.cuda.synchronize()
+    assert int(run.flag.item()) == 0
+
+    # Norm over the whole tiled gradient.
+    if w.pre_reduced:
+        reduced_period = period_grad
+    else:
+        reduced_period, bad = step.reduce_shard(period_contribs, w.grad_dtype)
+        assert not bad
+    sumsq = _period_sumsq(reduced_period, n % PERIOD, n, w.grad_dtype, w.inv_loss_scale)
+    norm = step.norm_from_sumsq(sumsq)
+    coef = step.clip_coef(norm, w.max_norm)
+    _note(f"  norm gpu {run.norm.item():.12g} oracle {norm:.12g}, coef {float(coef):.8g}")
+    assert run.norm.item() == pytest.approx(norm, rel=1e-5)
+    assert float(coef) < 1.0                                  # clipping is active
+
+    for o in offs:
+        contribs, grad, (p0, m0, v0) = chunks[o]
+        if contribs is not None:
+            reduced, bad = step.reduce_shard(contribs, w.grad_dtype)
+            assert not bad
+            assert np.array_equal(synth.bits(run.reduced[0, o:o + CHUNK]), reduced), f"reduced @ {o}"
+        else:
+            reduced = grad
+        p, m, v, bits = step.adam_update(p0, m0, v0, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
+        _state_ok(run.master[0, o:o + CHUNK].cpu().numpy(), p, f"master @ {o}")
+        _state_ok(run.m[0, o:o + CHUNK].cpu().numpy(), m, f"m @ {o}")
+        _state_ok(run.v[0, o:o + CHUNK].cpu().numpy(), v, f"v @ {o}")
+        _ulp_ok(synth.bits(run.param_out(0)[o:o + CHUNK]), bits, f"param @ {o}")
+        if others is not None:
+            # Gathered buffer: each owner's chunk lands at its unit/rank place.
+            got_own = synth.bits(run.param_out(0)[o:o + CHUNK])
+            for r in (0, 1, w.nd - 1):
+                src = got_own if r == w.rank else others[o][r]
+                for j in range(0, CHUNK, CHUNK // 4):
+                    e = o + j
+                    ui = max(i for i, u in enumerate(plan.units) if u.shard_base <= e)
+                    u = plan.units[ui]
+                    dst = u.full_base + r * u.slice_numel + (e - u.shard_base)
+                    seg = min(CHUNK // 4, u.shard_base + u.slice_numel - e)
+                    got = synth.bits(run.full[dst:dst + seg])
+                    assert np.array_equal(got, src[j:j + seg]), f"gather owner {r} @ {e}"
+        if w.stage in (1, 2) and not w.pre_reduced:
+            base = w.rank * n + o
+            assert np.array_equal(synth.bits(run.full[base:base + CHUNK]), synth.bits(run.param_out(0)[o:o + CHUNK]))
+    del run

@@ -20,7 +20,7 @@
 //                   fused per-block fp64 sums of squares and the inf/NaN flag
 //                   (L18 notes §2.2 step 3, §2.5).
 //   sumsq_kernel    a2: the same sums of squares over an already-reduced
-//                   gradient.
+//                   gradient, one 2048-element range per wave.
 //   finalize_kernel a2: fixed-order fp64 sum of the partials -> norm and the
 //                   clip multiplier (L18 notes §1.4; L3.2 §4.2).
 //   adam_kernel     a3: AdamW on fp32 master/m/v, cast to 16 bits (L18 notes
@@ -283,58 +283,73 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(Ptrs64 tab, const 
 // a2: sums of squares of a pre-reduced gradient, and the finalize
 // ---------------------------------------------------------------------------
 
+// Each 64-lane wave owns whole partial ranges (kPartialQuads quads, i.e. one
+// range of the reduce's partial sums) and sums each with a fixed shuffle tree;
+// a block of kSumsqWaves waves covers kSumsqWaves * kSumsqRangesPerWave
+// consecutive ranges, so a block streams enough bytes to keep HBM busy even
+// though the kernel reads a single array.
+constexpr int kSumsqWaves = 4;
+constexpr int kSumsqBlock = 64 * kSumsqWaves;
+constexpr int kSumsqRangesPerWave = 4;
+constexpr int kSumsqQuadsPerLane = int(kPartialQuads / 64);
+
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;  // every lane holds the total
+}
+
 template <int DT>
-__global__ __launch_bounds__(kReduceBlock) void sumsq_kernel(const uint16_t* __restrict__ g, Span sp,
-                                                       float inv_s, double* __restrict__ partials,
-                                                       int32_t* __restrict__ flag) {
-    double sq = 0.0;
+__global__ __launch_bounds__(kSumsqBlock) void sumsq_kernel(const uint16_t* __restrict__ g, Span sp,
+                                                            float inv_s, int64_t n_ranges,
+                                                            double* __restrict__ partials,
+                                                            int32_t* __restrict__ flag) {
+    static_assert(kPartialQuads % 64 == 0, "a range must split evenly over a wave");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int bad = 0;
-    auto add = [&](uint32_t b) {
+    auto term = [&](uint32_t b) -> double {
         bad |= !finite16<DT>(b);
         const double d = double(widen<DT>(b)) * double(inv_s);
-        sq += d * d;
+        return d * d;
     };
     const u2* qg = reinterpret_cast<const u2*>(g + sp.head);
-    if (sp.vec) {
-        const int64_t q0 = int64_t(blockIdx.x) * kPartialQuads + threadIdx.x;
-        for (int t = 0; t < kPartialTiles; ++t) {
-            const int64_t tq = q0 + int64_t(t) * kReduceTileQuads;
-            if (tq - threadIdx.x + kReduceTileQuads <= sp.nq) {
-                u2 w[kReduceQuadsPerLane];
+    const int64_t first = (int64_t(blockIdx.x) * kSumsqWaves + wave) * kSumsqRangesPerWave;
+    for (int j = 0; j < kSumsqRangesPerWave; ++j) {
+        const int64_t range = first + j;
+        if (range >= n_ranges) break;
+        double sq = 0.0;
+        if (sp.vec) {
+            const int64_t q0 = range * kPartialQuads + lane;
+            if (range * kPartialQuads + kPartialQuads <= sp.nq) {
+                u2 w[kSumsqQuadsPerLane];
 #pragma unroll
-                for (int u = 0; u < kReduceQuadsPerLane; ++u) w[u] = ld_stream(qg + tq + u * kReduceBlock);
+                for (int u = 0; u < kSumsqQuadsPerLane; ++u) w[u] = ld_stream(qg + q0 + u * 64);
 #pragma unroll
-                for (int u = 0; u < kReduceQuadsPerLane; ++u)
+                for (int u = 0; u < kSumsqQuadsPerLane; ++u)
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) add(half_of(w[u], k));
+                    for (int k = 0; k < 4; ++k) sq += term(half_of(w[u], k));
             } else {
-                for (int u = 0; u < kReduceQuadsPerLane; ++u) {
-                    const int64_t q = tq + u * kReduceBlock;
+                for (int u = 0; u < kSumsqQuadsPerLane; ++u) {
+                    const int64_t q = q0 + u * 64;
                     if (q >= sp.nq) break;
                     const u2 w = qg[q];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) add(half_of(w, k));
+                    for (int k = 0; k < 4; ++k) sq += term(half_of(w, k));
                 }
-                break;
             }
+            if (range == n_ranges - 1) {
+                const int64_t tail0 = sp.head + 4 * sp.nq;
+                const int64_t nscalar = sp.head + (sp.n - tail0);
+                for (int64_t k = lane; k < nscalar; k += 64) sq += term(g[k < sp.head ? k : tail0 + (k - sp.head)]);
+            }
+        } else {
+            const int64_t e0 = range * kPartialElems;
+            const int64_t e1 = e0 + kPartialElems < sp.n ? e0 + kPartialElems : sp.n;
+            for (int64_t e = e0 + lane; e < e1; e += 64) sq += term(g[e]);
         }
-        if (blockIdx.x == gridDim.x - 1) {
-            const int64_t tail0 = sp.head + 4 * sp.nq;
-            const int64_t nscalar = sp.head + (sp.n - tail0);
-            for (int64_t k = threadIdx.x; k < nscalar; k += kReduceBlock) add(g[k < sp.head ? k : tail0 + (k - sp.head)]);
-        }
-    } else {
-        const int64_t e0 = int64_t(blockIdx.x) * kPartialElems;
-        const int64_t e1 = e0 + kPartialElems < sp.n ? e0 + kPartialElems : sp.n;
-        for (int64_t e = e0 + threadIdx.x; e < e1; e += kReduceBlock) add(g[e]);
+        const double total = wave_sum(sq);
+        if (lane == 0) partials[range] = total;
     }
-
-    const double total = block_sum<kReduceBlock>(sq);
-    const int any_bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) {
-        partials[blockIdx.x] = total;
-        if (any_bad) atomicOr(flag, ZERO_FLAG_NONFINITE_GRAD);
-    }
+    if (__any(bad) && lane == 0) atomicOr(flag, ZERO_FLAG_NONFINITE_GRAD);
 }
 
 constexpr int kFinalizeBlock = 1024;
@@ -750,12 +765,13 @@ int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
         const void* p16[1] = {grad};
         const Span sp = make_span(n, p16, 1, nullptr, 0);
         const uint16_t* g16 = static_cast<const uint16_t*>(grad);
+        const dim3 grid{unsigned(ceil_div(blocks, int64_t(kSumsqWaves) * kSumsqRangesPerWave))};
         const hipError_t e =
             dtype == ZERO_F16
-                ? launch(sumsq_kernel<ZERO_F16>, dim3(unsigned(blocks)), dim3(kReduceBlock), s, g16, sp,
-                         inv_loss_scale, partials, flag)
-                : launch(sumsq_kernel<ZERO_BF16>, dim3(unsigned(blocks)), dim3(kReduceBlock), s, g16, sp,
-                         inv_loss_scale, partials, flag);
+                ? launch(sumsq_kernel<ZERO_F16>, grid, dim3(kSumsqBlock), s, g16, sp, inv_loss_scale, blocks,
+                         partials, flag)
+                : launch(sumsq_kernel<ZERO_BF16>, grid, dim3(kSumsqBlock), s, g16, sp, inv_loss_scale, blocks,
+                         partials, flag);
         if (e != hipSuccess) return hip_status(e, fn);
     }
     // With n = 0 every partial sum is zero by definition: none is read, so an
