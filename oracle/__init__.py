@@ -21,6 +21,8 @@ owned slice of the flat parameter vector:
   (4+K)Ψ/Nd and communication volume 2Ψ / 3Ψ × (Nd−1)/Nd (Lecture 18 notes
   §2.1, §3.1; L3.2 Memory optimisation and ZeRO §2.3).
 * ``rounding``   -- fp32 → bf16 / fp16 round-to-nearest-even.
+* ``quant``      -- block-quantised 16-bit parameters for the gather (ZeRO++
+  quantised weights; Lecture 18 notes §4.5): absmax INT8/INT4 per 256.
 * ``step``       -- the averaged reduce-scatter slice (Lecture 18 notes §2.2
   step 3), the exact global L2 norm and clip coefficient (Lecture 18 notes
   §1.4; L3.2 §4.2 ``gradient_clipping``), the Adam(W) update of the owned
@@ -44,7 +46,7 @@ published formulas they restate, through library routines
 ``"f16"`` or ``"bf16"``; fp32 state is ``numpy.float32``.
 """
 
-from . import accounting, partition, rounding, step  # noqa: F401
+from . import accounting, partition, quant, rounding, step  # noqa: F401
 from .accounting import comm_volume, max_params, model_state_bytes  # noqa: F401
 from .partition import Plan, make_plan, segments, shard_of  # noqa: F401
 from .rounding import narrow, widen  # noqa: F401

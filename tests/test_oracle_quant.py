@@ -1,0 +1,112 @@
+"""Pins for oracle.quant (block-quantised parameters for the gather).
+
+The page's experiment (CMU 11-868 Lecture 18 notes §4.5): 1M weights with 64
+values 20 times larger, quantised with one scale per tensor or per 256
+values.  The page does not state its distribution or error measure; under
+the reading N(0, 1) weights, 64 of them multiplied by 20, relative L2 error,
+the printed figures come out (see test_page_experiment).  The per-block and
+INT4 per-tensor figures barely move between seeds; INT8 per tensor depends on
+the largest outlier drawn, so it is checked as a range.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import quant, rounding
+
+
+def _f16(vals):
+    return rounding.narrow(np.asarray(vals, np.float32), "f16")
+
+
+def _experiment(seed):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal(1_000_000)
+    w[rng.choice(w.size, 64, replace=False)] *= 20
+    x = _f16(w)
+    errors = {}
+    for bits in (8, 4):
+        for block in (w.size, 256):
+            codes, scales = quant.quantize(x, "f16", bits, block)
+            back = quant.dequantize(codes, scales, "f16", block)
+            errors[(bits, block == 256)] = quant.relative_error(rounding.widen(x, "f16"),
+                                                                rounding.widen(back, "f16"))
+    return errors
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_page_experiment(seed):
+    e = _experiment(seed)
+    assert 0.0080 <= e[(8, True)] <= 0.0098            # printed 0.89%
+    assert 0.135 <= e[(4, True)] <= 0.155               # printed 14.53%
+    assert 0.970 <= e[(4, False)] <= 0.995              # printed 98.69%
+    assert 0.08 <= e[(8, False)] <= 0.17                # printed 11.25% (outlier-dependent)
+    assert e[(8, False)] > 8 * e[(8, True)]             # blocks win by an order of magnitude
+
+
+def test_page_experiment_seed0_close_to_print():
+    e = _experiment(0)
+    assert e[(8, True)] == pytest.approx(0.0089, abs=0.0003)
+    assert e[(4, False)] == pytest.approx(0.9869, abs=0.003)
+    assert e[(4, True)] == pytest.approx(0.1453, abs=0.005)
+    assert e[(8, False)] == pytest.approx(0.1125, abs=0.005)
+
+
+def test_int8_hand_worked_ties():
+    # Block maximum 127 gives scale exactly 1: codes are the rounded values,
+    # ties to even (63.5 -> 64, 2.5 -> 2, -3.5 -> -4).
+    x = _f16([63.5, -127.0, 2.5, -3.5, 0.0, 1.25])
+    codes, scales = quant.quantize(x, "f16", 8)
+    assert scales.tolist() == [1.0]
+    assert codes.tolist() == [64, -127, 2, -4, 0, 1]
+    assert rounding.widen(quant.dequantize(codes, scales, "f16"), "f16").tolist() == [64, -127, 2, -4, 0, 1]
+
+
+def test_int4_hand_worked():
+    x = _f16([7.0, -6.5, 0.5, 1.5, -7.0])
+    codes, scales = quant.quantize(x, "f16", 4)
+    assert scales.tolist() == [1.0]
+    assert codes.tolist() == [7, -6, 0, 2, -7]
+
+
+def test_zero_block_and_ragged_tail():
+    x = np.concatenate([_f16(np.zeros(256)), _f16(np.linspace(-1, 1, 100))])
+    codes, scales = quant.quantize(x, "f16", 8)
+    assert scales.shape == (2,) and scales[0] == 0 and np.all(codes[:256] == 0)
+    assert scales[1] == np.float32(np.float32(1.0) / np.float32(127))
+    back = rounding.widen(quant.dequantize(codes, scales, "f16"), "f16")
+    assert np.all(back[:256] == 0)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_round_trip_error_bound(bits, dtype):
+    # |x' - x| <= scale/2 per element, plus the 16-bit rounding of the result.
+    rng = np.random.default_rng(bits)
+    x = rounding.narrow((rng.standard_normal(10_000) * 0.02).astype(np.float32), dtype)
+    codes, scales = quant.quantize(x, dtype, bits)
+    assert codes.min() >= -quant.QMAX[bits] and codes.max() <= quant.QMAX[bits]
+    back = rounding.widen(quant.dequantize(codes, scales, dtype), dtype).astype(np.float64)
+    xv = rounding.widen(x, dtype).astype(np.float64)
+    per = np.repeat(scales.astype(np.float64), 256)[:x.size]
+    ulp16 = 2.0 ** -10 if dtype == "f16" else 2.0 ** -7
+    assert np.all(np.abs(back - xv) <= per / 2 + np.abs(back) * ulp16 + 1e-30)
+    # the element with the block maximum is represented exactly up to rounding
+    blocks = np.abs(xv[:9984]).reshape(-1, 256).argmax(axis=1) + np.arange(39) * 256
+    assert np.all(np.abs(np.abs(back[blocks]) - np.abs(xv[blocks])) <= np.abs(xv[blocks]) * 2 * ulp16)
+
+
+def test_pack4_round_trip():
+    codes = np.array(list(range(-7, 8)) + [3], np.int8)
+    packed = quant.pack4(codes)
+    assert packed.dtype == np.uint8 and packed.shape == (8,)
+    assert packed[0] == ((-7 & 0xF) | ((-6 & 0xF) << 4))
+    assert np.array_equal(quant.unpack4(packed, codes.size), codes)
+    odd = codes[:15]
+    assert np.array_equal(quant.unpack4(quant.pack4(odd), 15), odd)
+    assert quant.pack4(odd)[-1] >> 4 == 0
+
+
+def test_bad_bits():
+    with pytest.raises(ValueError):
+        quant.quantize(_f16([1.0]), "f16", 2)
