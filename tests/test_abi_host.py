@@ -195,3 +195,36 @@ def test_gather_rejects():
             abi.zero_gather_params(**dict(base, **bad))
         assert e.value.code == code
     abi.zero_gather_params(**dict(base, unit_begin=1, unit_end=1))   # empty range: no-op
+
+
+def test_quant_sizes():
+    assert abi.zero_quant_code_bytes(1000, 8) == 1000
+    assert abi.zero_quant_code_bytes(1001, 4) == 501
+    assert abi.zero_quant_scale_count(0) == 0
+    assert abi.zero_quant_scale_count(257) == 2
+    with pytest.raises(abi.ZeroError):
+        abi.zero_quant_code_bytes(10, 3)
+
+
+def test_quant_rejects():
+    for bad, code in ((dict(bits=3), abi.ZERO_EINVAL), (dict(dtype=5), abi.ZERO_EINVAL), (dict(x=A + 2), abi.ZERO_EINVAL),
+                      (dict(codes=A + 1000), abi.ZERO_EALIAS), (dict(scales=A + 100), abi.ZERO_EALIAS)):
+        args = dict(x=A, dtype=1, n=1000, bits=8, codes=B, scales=W, stream=0)
+        args.update(bad)
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_quantize_blocks(**args)
+        assert e.value.code == code
+    with pytest.raises(abi.ZeroError):
+        abi.zero_dequantize_blocks(B, W, 1000, 8, A + 4, 1, stream=0)      # y misaligned
+    abi.zero_quantize_blocks(None, 1, 0, 8, None, None, stream=0)          # n = 0: no-op
+
+
+def test_gather_dequant_rejects():
+    plan = abi.Plan([4096, 2048], 4, 3, 8)                 # align 8: blocks could straddle
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_gather_dequant(plan, [A] * 4, [W] * 4, 0, 2, 8, 1, B, stream=0)
+    assert e.value.code == abi.ZERO_EINVAL
+    plan = abi.Plan([4096, 2048], 4, 3, 256)
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_gather_dequant(plan, [A] * 4, [W] * 4, 0, 2, 8, 1, B + 2, stream=0)   # full misaligned
+    assert e.value.code == abi.ZERO_EINVAL

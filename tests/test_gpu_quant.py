@@ -1,0 +1,149 @@
+"""GPU parity of the block-quantised parameter gather against the oracle.
+
+Codes and scales are decisions taken in float32 on both sides (IEEE division,
+round half to even), so they are compared bit for bit, as are the
+dequantised 16-bit values and the gathered buffer.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import partition, quant, rounding, step
+
+pytestmark = pytest.mark.gpu
+
+TORCH16 = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def abi():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_sharded_mixed_flat_amd import abi as _abi
+    return _abi
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def _params(rng, n, dtype, outliers=True):
+    w = rng.standard_normal(n) * 0.02
+    if outliers and n > 10:
+        w[rng.choice(n, max(1, n // 10000), replace=False)] *= 20
+    return rounding.narrow(w.astype(np.float32), dtype)
+
+
+def _dev16(bits, dtype):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH16[dtype]).cuda()
+
+
+def _bits(t):
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _host_codes(codes, bits, n):
+    raw = codes.cpu().numpy().view(np.uint8)
+    return raw[:n].view(np.int8) if bits == 8 else quant.unpack4(raw, n)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 3, 255, 256, 257, 1000, 65543, 1_000_003])
+def test_quantize_dequantize(abi, bits, dtype, n):
+    _note(f"quantize bits={bits} dtype={dtype} n={n}")
+    rng = np.random.default_rng(n * 7 + bits)
+    x = _params(rng, n, dtype)
+    ref_codes, ref_scales = quant.quantize(x, dtype, bits)
+    ref_back = quant.dequantize(ref_codes, ref_scales, dtype)
+    dx = _dev16(x, dtype)
+    codes = torch.zeros(abi.zero_quant_code_bytes(n, bits) + 4, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(abi.zero_quant_scale_count(n), dtype=torch.float32, device="cuda")
+    back = torch.zeros(n, dtype=TORCH16[dtype], device="cuda")
+    abi.zero_quantize_blocks(dx, dtype, n, bits, codes, scales)
+    abi.zero_dequantize_blocks(codes, scales, n, bits, back, dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    assert np.array_equal(_host_codes(codes, bits, n), ref_codes)
+    if bits == 4:
+        assert np.array_equal(codes.cpu().numpy()[:(n + 1) // 2], quant.pack4(ref_codes))
+    assert np.array_equal(_bits(back), ref_back)
+    assert np.all(codes.cpu().numpy()[abi.zero_quant_code_bytes(n, bits):] == 0)   # nothing past the end
+
+
+def test_zero_blocks_and_ties(abi):
+    x = np.concatenate([rounding.narrow(np.zeros(256, np.float32), "f16"),
+                        rounding.narrow(np.array([63.5, -127.0, 2.5, -3.5] * 64, np.float32), "f16")])
+    codes = torch.zeros(512, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(2, dtype=torch.float32, device="cuda")
+    abi.zero_quantize_blocks(_dev16(x, "f16"), "f16", 512, 8, codes, scales)
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy().view(np.int8)
+    assert scales.cpu().tolist() == [0.0, 1.0]
+    assert np.all(c[:256] == 0) and c[256:260].tolist() == [64, -127, 2, -4]
+
+
+def test_page_experiment_on_gpu(abi):
+    # 1M weights, 64 of them x20: per-256 INT8 and INT4 errors as on the page.
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal(1_000_000)
+    w[rng.choice(w.size, 64, replace=False)] *= 20
+    x = rounding.narrow(w.astype(np.float32), "f16")
+    dx = _dev16(x, "f16")
+    errs = {}
+    for bits in (8, 4):
+        codes = torch.empty(abi.zero_quant_code_bytes(w.size, bits), dtype=torch.uint8, device="cuda")
+        scales = torch.empty(abi.zero_quant_scale_count(w.size), dtype=torch.float32, device="cuda")
+        back = torch.empty(w.size, dtype=torch.float16, device="cuda")
+        abi.zero_quantize_blocks(dx, "f16", w.size, bits, codes, scales)
+        abi.zero_dequantize_blocks(codes, scales, w.size, bits, back, "f16")
+        torch.cuda.synchronize()
+        errs[bits] = quant.relative_error(rounding.widen(x, "f16"), rounding.widen(_bits(back), "f16"))
+    assert errs[8] == pytest.approx(0.0089, abs=0.0003)      # printed 0.89%
+    assert errs[4] == pytest.approx(0.1453, abs=0.005)       # printed 14.53%
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("units, nd", [([70_000, 1234, 99_999], 4), ([4096] * 3, 64), ([300_001], 100)])
+def test_gather_dequant(abi, bits, units, nd):
+    _note(f"gather_dequant bits={bits} units={units} nd={nd}")
+    dtype = "bf16"
+    plan = abi.Plan(units, nd, 3, 256)
+    ref_plan = partition.make_plan(units, nd, 3, 256)
+    n = ref_plan.shard_numel
+    rng = np.random.default_rng(nd + bits)
+    shards = [_params(rng, n, dtype) for _ in range(nd)]
+    code_dev, scale_dev, deq = [], [], []
+    for sh in shards:
+        c, sc = quant.quantize(sh, dtype, bits)
+        deq.append(quant.dequantize(c, sc, dtype))
+        raw = c.view(np.uint8) if bits == 8 else quant.pack4(c)
+        code_dev.append(torch.from_numpy(raw.copy()).cuda())
+        scale_dev.append(torch.from_numpy(sc.copy()).cuda())
+    full = torch.full((ref_plan.full_numel,), 0.5, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(abi.zero_workspace_bytes(0, 0), dtype=torch.uint8, device="cuda")
+    abi.zero_gather_dequant(plan, code_dev, scale_dev, 0, len(units), bits, dtype, full, ws)
+    torch.cuda.synchronize()
+    expect = step.gather(ref_plan, deq, np.full(ref_plan.full_numel, 0x3F00, np.uint16))   # 0.5 in bf16
+    assert np.array_equal(_bits(full), expect)
+
+
+def test_quantize_then_gather_chain(abi):
+    # The sending side (GPU quantise) feeding the receiving side (GPU gather).
+    units, nd, bits, dtype = [50_000, 7_777], 8, 8, "f16"
+    plan = abi.Plan(units, nd, 3, 256)
+    ref_plan = partition.make_plan(units, nd, 3, 256)
+    n = ref_plan.shard_numel
+    rng = np.random.default_rng(5)
+    shards = [_params(rng, n, dtype) for _ in range(nd)]
+    codes = [torch.empty(abi.zero_quant_code_bytes(n, bits), dtype=torch.uint8, device="cuda") for _ in range(nd)]
+    scales = [torch.empty(abi.zero_quant_scale_count(n), dtype=torch.float32, device="cuda") for _ in range(nd)]
+    for sh, c, s in zip(shards, codes, scales):
+        abi.zero_quantize_blocks(_dev16(sh, dtype), dtype, n, bits, c, s)
+    full = torch.zeros(ref_plan.full_numel, dtype=torch.float16, device="cuda")
+    abi.zero_gather_dequant(plan, codes, scales, 0, len(units), bits, dtype, full)
+    torch.cuda.synchronize()
+    deq = [quant.dequantize(*quant.quantize(sh, dtype, bits), dtype) for sh in shards]
+    expect = step.gather(ref_plan, deq, np.zeros(ref_plan.full_numel, np.uint16))
+    assert np.array_equal(_bits(full), expect)

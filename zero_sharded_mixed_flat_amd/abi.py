@@ -35,7 +35,10 @@ EXPORTED = (
     "zero_plan_full_numel", "zero_plan_segments", "zero_model_state_bytes", "zero_comm_volume",
     "zero_workspace_bytes", "zero_reduce_shard", "zero_grad_norm", "zero_adam_step",
     "zero_gather_params", "zero_last_error", "zero_version",
+    "zero_quant_code_bytes", "zero_quant_scale_count", "zero_quantize_blocks", "zero_dequantize_blocks",
+    "zero_gather_dequant",
 )
+ZERO_QBLOCK = 256
 
 
 class ZeroError(RuntimeError):
@@ -84,6 +87,11 @@ _sig = {
     "zero_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
                             _P]),
     "zero_gather_params": (_I, [_P, ctypes.POINTER(_P), _I, _I, _I, _P, _P, _I64, _P]),
+    "zero_quant_code_bytes": (_I64, [_I64, _I]),
+    "zero_quant_scale_count": (_I64, [_I64]),
+    "zero_quantize_blocks": (_I, [_P, _I, _I64, _I, _P, _P, _P]),
+    "zero_dequantize_blocks": (_I, [_P, _P, _I64, _I, _P, _I, _P]),
+    "zero_gather_dequant": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _I, _I, _I, _P, _P, _I64, _P]),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_version": (_I, []),
 }
@@ -296,3 +304,59 @@ def zero_gather_params(plan, shards, unit_begin, unit_end, dtype, full, workspac
         _need(full, 2 * plan.full_numel(), "full")
     _check(lib.zero_gather_params(handle, ptrs, int(unit_begin), int(unit_end), _dtype(dtype),
                                   _ptr(full), _ptr(workspace), wb, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# block-quantised parameter gather
+# ---------------------------------------------------------------------------
+
+def zero_quant_code_bytes(n, bits):
+    b = lib.zero_quant_code_bytes(int(n), int(bits))
+    if b < 0:
+        raise ZeroError(ZERO_EINVAL, zero_last_error())
+    return b
+
+
+def zero_quant_scale_count(n):
+    c = lib.zero_quant_scale_count(int(n))
+    if c < 0:
+        raise ZeroError(ZERO_EINVAL, zero_last_error())
+    return c
+
+
+def zero_quantize_blocks(x, dtype, n, bits, codes, scales, stream=None):
+    if n > 0 and bits in (8, 4):
+        _need(x, 2 * n, "x")
+        _need(codes, zero_quant_code_bytes(n, bits), "codes")
+        _need(scales, 4 * zero_quant_scale_count(n), "scales")
+    _check(lib.zero_quantize_blocks(_ptr(x), _dtype(dtype), int(n), int(bits), _ptr(codes), _ptr(scales),
+                                    _stream(stream)))
+
+
+def zero_dequantize_blocks(codes, scales, n, bits, y, dtype, stream=None):
+    if n > 0 and bits in (8, 4):
+        _need(codes, zero_quant_code_bytes(n, bits), "codes")
+        _need(scales, 4 * zero_quant_scale_count(n), "scales")
+        _need(y, 2 * n, "y")
+    _check(lib.zero_dequantize_blocks(_ptr(codes), _ptr(scales), int(n), int(bits), _ptr(y), _dtype(dtype),
+                                      _stream(stream)))
+
+
+def zero_gather_dequant(plan, code_shards, scale_shards, unit_begin, unit_end, bits, dtype, full, workspace=None,
+                        stream=None, workspace_bytes=None):
+    cp = (_P * len(code_shards))(*[_ptr(c) for c in code_shards])
+    sp = (_P * len(scale_shards))(*[_ptr(c) for c in scale_shards])
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    handle = plan.handle if isinstance(plan, Plan) else plan
+    if isinstance(plan, Plan):
+        owners = plan.info()["owners"]
+        if len(code_shards) != owners or len(scale_shards) != owners:
+            raise ValueError(f"need {owners} code and scale shards")
+        shard_numel, _ = plan.rank(0)
+        if bits in (8, 4):
+            for i in range(owners):
+                _need(code_shards[i], zero_quant_code_bytes(shard_numel, bits), f"code shard {i}")
+                _need(scale_shards[i], 4 * zero_quant_scale_count(shard_numel), f"scale shard {i}")
+        _need(full, 2 * plan.full_numel(), "full")
+    _check(lib.zero_gather_dequant(handle, cp, sp, int(unit_begin), int(unit_end), int(bits), _dtype(dtype),
+                                   _ptr(full), _ptr(workspace), wb, _stream(stream)))

@@ -36,13 +36,16 @@ def build(verbose=True):
     os.makedirs(objdir, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
     plan_o = os.path.join(objdir, "plan.o")
-    kern_o = os.path.join(objdir, "kernels.o")
     _run([hipcc, *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
-    _run([hipcc, *common, "-x", "hip", f"--offload-arch={ARCH}",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
+    objs = [plan_o]
+    for src in ("kernels.hip", "quant.hip"):
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        _run([hipcc, *common, "-x", "hip", f"--offload-arch={ARCH}",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", plan_o, kern_o, "-o", tmp])
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 
