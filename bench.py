@@ -3,7 +3,8 @@
 A step is the whole hot path over one batch of resident synthetic inputs:
 reduce the rank's slice from its Nd contributions (with fused norm partials),
 finalize the global norm and clip multiplier, run AdamW on the fp32 shard and
-write the 16-bit parameters (plus the per-layer gather for ZeRO-3 workloads).
+write the 16-bit parameters (plus the per-layer gather for ZeRO-3 workloads,
+plain or block-quantised).
 
 Prints ONE JSON line.  ``value`` is parameters updated per second by this GPU
 (the whole job at one GPU).  ``roofline`` reports the dominant kernel (the
@@ -65,6 +66,7 @@ def cpu_baseline(run, budget_s=12.0):
     import numpy as np
 
     from oracle import partition
+    from oracle import quant as oquant
     from oracle import step as ostep
     from oracle.step import AdamHparams
     from zero_sharded_mixed_flat_amd import synth
@@ -91,8 +93,14 @@ def cpu_baseline(run, budget_s=12.0):
             reduced = grad
         norm = ostep.norm_from_sumsq(ostep.sumsq_exact(reduced, w.grad_dtype, w.inv_loss_scale))
         coef = ostep.clip_coef(norm, w.max_norm)
-        ostep.adam_update(master, m, v, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
-        if w.gather_per_unit:
+        _, _, _, param = ostep.adam_update(master, m, v, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
+        if w.gather_bits != 16:
+            # quantise the owned chunk once, dequantise every rank's codes into the sample layout
+            codes, scales = oquant.quantize(param, w.param_dtype, w.gather_bits)
+            full = np.empty(chunk * w.nd, np.uint16)
+            for r in range(w.nd):
+                full[r * chunk:(r + 1) * chunk] = oquant.dequantize(codes, scales, w.param_dtype)
+        elif w.gather_per_unit:
             # the gather, on a one-unit sample layout whose slices are `chunk` long
             sample_plan = partition.make_plan([chunk * w.nd], w.nd, 3, 1)
             ostep.gather(sample_plan, [reduced] * w.nd, np.empty(chunk * w.nd, np.uint16))
@@ -109,9 +117,15 @@ def cpu_baseline(run, budget_s=12.0):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{reps} x {chunk} owned elements of this workload's inputs (reduce over {w.nd} ranks, "
-                  f"exact norm, AdamW{', gather' if w.gather_per_unit else ''}), single-threaded numpy",
+                  f"exact norm, AdamW{_gather_label(w)}), single-threaded numpy",
         "seconds": round(dt, 3),
     }, parity
+
+
+def _gather_label(w):
+    if w.gather_bits != 16:
+        return f", INT{w.gather_bits} quantise + {w.nd} dequantising gathers"
+    return ", gather" if w.gather_per_unit else ""
 
 
 def _short(name):
@@ -255,7 +269,7 @@ def main():
 
     # Per-kernel durations: HIP events on the stream the kernels are launched on.
     stream = torch.cuda.current_stream()
-    phases = ["reduce", "norm", "adam", "gather"]
+    phases = ["reduce", "norm", "adam", "quantize", "gather"]
     acc = {p: 0.0 for p in phases}
     for _ in range(args.steps):
         ev = {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for p in phases}
@@ -270,6 +284,10 @@ def main():
         ev["adam"][0].record(stream)
         run.adam_all()
         ev["adam"][1].record(stream)
+        if run.codes is not None:
+            ev["quantize"][0].record(stream)
+            run.quantize_all()
+            ev["quantize"][1].record(stream)
         if run.shards is not None:
             ev["gather"][0].record(stream)
             run.gather_all()
@@ -277,7 +295,8 @@ def main():
         run.t += 1
         torch.cuda.synchronize()
         for p in phases:
-            if p == "reduce" and w.pre_reduced or p == "gather" and run.shards is None:
+            if (p == "reduce" and w.pre_reduced or p == "gather" and run.shards is None
+                    or p == "quantize" and run.codes is None):
                 continue
             acc[p] += ev[p][0].elapsed_time(ev[p][1])
     kern_ms = {p: acc[p] / args.steps for p in phases}

@@ -315,9 +315,9 @@ int zero_dequantize_blocks(const void* codes, const float* scales, int64_t n, in
  * where code_shards[r] / scale_shards[r] hold owner r's whole shard quantised
  * with zero_quantize_blocks.  The plan's align must be a multiple of
  * ZERO_QBLOCK so blocks never straddle units or owners.  code_shards and
- * scale_shards are HOST arrays of `owners` device pointers (codes 4-byte
+ * scale_shards are HOST arrays of `owners` device pointers (codes 16-byte
  * aligned, scales 4-byte aligned); full is the padded full 16-bit buffer,
- * 8-byte aligned.  workspace: >= zero_workspace_bytes(0, 0) bytes when there
+ * 16-byte aligned (device allocations are).  workspace: >= zero_workspace_bytes(0, 0) bytes when there
  * are more than 64 owners (pointer tables), else may be NULL.
  */
 int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards,

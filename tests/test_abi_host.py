@@ -228,3 +228,9 @@ def test_gather_dequant_rejects():
     with pytest.raises(abi.ZeroError) as e:
         abi.zero_gather_dequant(plan, [A] * 4, [W] * 4, 0, 2, 8, 1, B + 2, stream=0)   # full misaligned
     assert e.value.code == abi.ZERO_EINVAL
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_gather_dequant(plan, [A] * 4, [W] * 4, 0, 2, 8, 1, B + 8, stream=0)   # full not 16-byte aligned
+    assert e.value.code == abi.ZERO_EINVAL
+    with pytest.raises(abi.ZeroError) as e:
+        abi.zero_gather_dequant(plan, [A, A + 8, A, A], [W] * 4, 0, 2, 8, 1, B, stream=0)   # codes not 16-aligned
+    assert e.value.code == abi.ZERO_EINVAL and "shard 1" in str(e.value)

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import partition, rounding, step
+from oracle import partition, quant, rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth, workloads
 
@@ -59,12 +59,66 @@ def _ulp_ok(got, ref, what):
     assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} params more than 1 ulp apart"
 
 
-def _offsets(n, extra=(), seed=0):
+def _offsets(n, extra=(), seed=0, align=1):
     rng = np.random.default_rng(seed)
-    offs = {0, max(0, n - CHUNK)}
-    offs.update(int(x) for x in rng.integers(0, max(1, n - CHUNK), size=6))
-    offs.update(min(max(0, int(x)), max(0, n - CHUNK)) for x in extra)
+    last = max(0, n - CHUNK) // align * align
+    offs = {0, last}
+    offs.update(int(x) // align * align for x in rng.integers(0, max(1, n - CHUNK), size=6))
+    offs.update(min(max(0, int(x)), last) // align * align for x in extra)
     return sorted(offs)
+
+
+def _gathered(run, plan, r, o):
+    """The full buffer's copy of owner r's shard elements [o, o + CHUNK)."""
+    out = []
+    e = o
+    while e < o + CHUNK:
+        u = max((u for u in plan.units if u.shard_base <= e), key=lambda u: u.shard_base)
+        seg = min(o + CHUNK - e, u.shard_base + u.slice_numel - e)
+        dst = u.full_base + r * u.slice_numel + (e - u.shard_base)
+        out.append(synth.bits(run.full[dst:dst + seg]))
+        e += seg
+    return np.concatenate(out)
+
+
+def _codes_at(run, r, o, bits):
+    """Owner r's codes for shard elements [o, o + CHUNK) (o a multiple of 256) as int8."""
+    lo, hi = o * bits // 8, (o + CHUNK) * bits // 8
+    raw = run.codes[r, lo:hi].cpu().numpy()
+    return raw.view(np.int8) if bits == 8 else quant.unpack4(raw, CHUNK)
+
+
+def _check_quantised_gather(run, plan, w, o, others, own_bits):
+    """Codes, scales and the dequantised full buffer for three owners at chunk o.
+
+    Other owners' shards are synthetic inputs: their codes, scales and gathered
+    values are compared bit for bit with the oracle's quantise/dequantise.  The
+    rank's own shard comes out of the AdamW step, where the 16-bit parameter may
+    sit one ulp from the oracle's; a block whose absmax element moved gets a
+    different scale, so its values are checked to within one quantisation step.
+    """
+    bits, dt = w.gather_bits, w.param_dtype
+    for r in (0, 1, w.nd - 1):
+        src = own_bits if r == w.rank else others[o][r]
+        codes, scales = quant.quantize(src, dt, bits)
+        expect = quant.dequantize(codes, scales, dt)
+        got = _gathered(run, plan, r, o)
+        if r != w.rank:
+            assert np.array_equal(run.scales[r, o // 256:(o + CHUNK) // 256].cpu().numpy(), scales), f"scales {r} @ {o}"
+            assert np.array_equal(_codes_at(run, r, o, bits), codes), f"codes {r} @ {o}"
+            assert np.array_equal(got, expect), f"dequantised gather, owner {r} @ {o}"
+            continue
+        # the own shard's codes decode to exactly what was gathered
+        own_scales = run.scales[r, o // 256:(o + CHUNK) // 256].cpu().numpy()
+        assert np.array_equal(got, quant.dequantize(_codes_at(run, r, o, bits), own_scales, dt))
+        gv, ev = rounding.widen(got, dt).astype(np.float64), rounding.widen(expect, dt).astype(np.float64)
+        step_size = np.repeat(scales.astype(np.float64), 256)
+        ulp16 = 2.0 ** (-10 if dt == "f16" else -7)
+        assert np.all(np.abs(gv - ev) <= step_size * 1.001 + (np.abs(gv) + np.abs(ev)) * ulp16), f"own gather @ {o}"
+        differ = got != expect
+        blocks = int(np.count_nonzero(differ.reshape(-1, 256).any(axis=1)))
+        _note(f"  own gather @ {o}: {int(differ.sum())} values in {blocks} blocks differ from the oracle's")
+        assert differ.mean() <= 0.02, f"own gather @ {o}: {differ.mean():.2%} of values differ"
 
 
 def _period_sumsq(reduced_period, tail_len, n, dtype, inv_s):
@@ -75,7 +129,7 @@ def _period_sumsq(reduced_period, tail_len, n, dtype, inv_s):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_nd8_z2", "gpt2_1p5b_nd16_z1", "paper_7p5b_nd64_z3",
-                                  "gpt3_175b_nd16_z1"])
+                                  "paper_7p5b_nd64_z3_qwz8", "paper_7p5b_nd64_z3_qwz4", "gpt3_175b_nd16_z1"])
 def test_full_size_step(runner, name):
     w = workloads.get(name)
     _note(f"full-size {name}: allocating")
@@ -85,7 +139,8 @@ def test_full_size_step(runner, name):
     assert n == plan.shard_numel
     hp = _hp(w)
     unit_edges = [u.shard_base for u in plan.units[1:]] if w.stage == 3 else []
-    offs = _offsets(n, extra=[e - CHUNK // 2 for e in unit_edges[:4]], seed=len(name))
+    offs = _offsets(n, extra=[e - CHUNK // 2 for e in unit_edges[:4]], seed=len(name),
+                    align=256 if w.gather_bits != 16 else 1)
 
     # Inputs, copied back before the step.
     def grads_at(lo, hi):
@@ -135,7 +190,9 @@ def test_full_size_step(runner, name):
         _state_ok(run.m[0, o:o + CHUNK].cpu().numpy(), m, f"m @ {o}")
         _state_ok(run.v[0, o:o + CHUNK].cpu().numpy(), v, f"v @ {o}")
         _ulp_ok(synth.bits(run.param_out(0)[o:o + CHUNK]), bits, f"param @ {o}")
-        if others is not None:
+        if run.codes is not None:
+            _check_quantised_gather(run, plan, w, o, others, bits)
+        elif others is not None:
             # Gathered buffer: each owner's chunk lands at its unit/rank place.
             got_own = synth.bits(run.param_out(0)[o:o + CHUNK])
             for r in (0, 1, w.nd - 1):

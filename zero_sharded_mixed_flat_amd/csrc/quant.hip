@@ -175,10 +175,43 @@ struct ScalePtrs64 {
     const float* p[64];
 };
 
-// Block (x, r) writes tile x of owner r's slice.  The slice and the unit's
-// shard base are multiples of 256, so every quad is whole and in one block.
+// Eight codes (an "oct") starting at element e, a multiple of 8: 8 bytes of
+// INT8 codes or 4 bytes of INT4 nibbles.  Lanes take consecutive octs, so each
+// load and each 16-byte store of a wave covers one contiguous span.
+template <int BITS>
+struct OctCodes;
+template <>
+struct OctCodes<8> {
+    u2 w;
+    __device__ __forceinline__ void load(const uint8_t* codes, int64_t e) {
+        w = ld_stream(reinterpret_cast<const u2*>(codes + e));
+    }
+    __device__ __forceinline__ int get(int k) const {  // sign-extended byte k
+        const uint32_t word = k < 4 ? w.x : w.y;
+        return static_cast<int>(word << (24 - 8 * (k & 3))) >> 24;
+    }
+};
+template <>
+struct OctCodes<4> {
+    uint32_t w;
+    __device__ __forceinline__ void load(const uint8_t* codes, int64_t e) {
+        w = ld_stream(reinterpret_cast<const uint32_t*>(codes + e / 2));
+    }
+    __device__ __forceinline__ int get(int k) const {  // sign-extended nibble k
+        return static_cast<int>(w << (28 - 4 * k)) >> 28;
+    }
+};
+
+constexpr int kGDThreads = 256;
+constexpr int kGDOctsPerLane = 4;
+constexpr int64_t kGDTileOcts = int64_t(kGDThreads) * kGDOctsPerLane;
+
+// Block (x, r) writes tile x of owner r's slice of one unit.  The slice and
+// the unit's shard base are multiples of 256, so every oct is whole and lies
+// in one quantisation block; the code shards and the full buffer are 16-byte
+// aligned.  All loads of a lane are issued before the first store.
 template <int DT, int BITS, bool DEVICE_TABLE>
-__global__ __launch_bounds__(kDeqThreads) void gather_dequant_kernel(
+__global__ __launch_bounds__(kGDThreads) void gather_dequant_kernel(
     CodePtrs64 ctab, ScalePtrs64 stab, const uint8_t* const* dctab, const float* const* dstab, int64_t slice,
     int64_t shard_base, int64_t full_base, uint16_t* __restrict__ full) {
     const int r = blockIdx.y;
@@ -192,19 +225,26 @@ __global__ __launch_bounds__(kDeqThreads) void gather_dequant_kernel(
         scales = stab.p[r];
     }
     uint16_t* dst = full + full_base + int64_t(r) * slice;
-    const int64_t q0 = int64_t(blockIdx.x) * kDeqTileQuads + threadIdx.x;
+    const int64_t q0 = int64_t(blockIdx.x) * kGDTileOcts + threadIdx.x;
+    OctCodes<BITS> c[kGDOctsPerLane];
+    float sc[kGDOctsPerLane];
 #pragma unroll
-    for (int u = 0; u < kDeqQuadsPerLane; ++u) {
-        const int64_t j = 4 * (q0 + u * kDeqThreads);
+    for (int u = 0; u < kGDOctsPerLane; ++u) {
+        const int64_t j = 8 * (q0 + u * kGDThreads);
+        if (j < slice) {
+            c[u].load(codes, shard_base + j);
+            sc[u] = scales[(shard_base + j) / kQBlock];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kGDOctsPerLane; ++u) {
+        const int64_t j = 8 * (q0 + u * kGDThreads);
         if (j >= slice) break;
-        const int64_t e = shard_base + j;
-        const float scale = scales[e / kQBlock];
-        int q[4];
-        load_codes4<BITS>(codes, e, q);
-        uint32_t o[4];
+        uint32_t h[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = narrow<DT>(float(q[k]) * scale);
-        st_stream(reinterpret_cast<u2*>(dst + j), pack4(o));
+        for (int k = 0; k < 8; ++k) h[k] = narrow<DT>(float(c[u].get(k)) * sc[u]);
+        st_stream(reinterpret_cast<u4*>(dst + j), u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                     h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
     }
 }
 
@@ -231,9 +271,9 @@ hipError_t launch_gather_dequant(bool device_table, dim3 grid, hipStream_t s, co
                                  const ScalePtrs64& st, const uint8_t* const* dct, const float* const* dst,
                                  int64_t slice, int64_t shard_base, int64_t full_base, uint16_t* full) {
     if (device_table)
-        return launch(gather_dequant_kernel<DT, BITS, true>, grid, dim3(kDeqThreads), s, ct, st, dct, dst, slice,
+        return launch(gather_dequant_kernel<DT, BITS, true>, grid, dim3(kGDThreads), s, ct, st, dct, dst, slice,
                       shard_base, full_base, full);
-    return launch(gather_dequant_kernel<DT, BITS, false>, grid, dim3(kDeqThreads), s, ct, st, dct, dst, slice,
+    return launch(gather_dequant_kernel<DT, BITS, false>, grid, dim3(kGDThreads), s, ct, st, dct, dst, slice,
                   shard_base, full_base, full);
 }
 
@@ -319,12 +359,12 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards, c
         return fail(ZERO_EINVAL, std::string(fn) + ": the plan's align must be a multiple of 256");
     if (unit_begin == unit_end) return ok();
     const int owners = plan->owners;
-    if (code_shards == nullptr || scale_shards == nullptr || full == nullptr || (addr(full) & 7))
-        return fail(ZERO_EINVAL, std::string(fn) + ": NULL argument or full not 8-byte aligned");
+    if (code_shards == nullptr || scale_shards == nullptr || full == nullptr || (addr(full) & 15))
+        return fail(ZERO_EINVAL, std::string(fn) + ": NULL argument or full not 16-byte aligned");
     const int64_t cb = code_bytes(plan->shard_numel, bits), sb = 4 * ceil_div(plan->shard_numel, kQBlock);
     const int64_t full_bytes = 2 * plan->full_numel;
     for (int r = 0; r < owners; ++r) {
-        if (code_shards[r] == nullptr || (addr(code_shards[r]) & 3) || scale_shards[r] == nullptr ||
+        if (code_shards[r] == nullptr || (addr(code_shards[r]) & 15) || scale_shards[r] == nullptr ||
             (addr(scale_shards[r]) & 3))
             return fail(ZERO_EINVAL, std::string(fn) + ": shard " + std::to_string(r) + " NULL or misaligned");
         if (overlaps(code_shards[r], cb, full, full_bytes) || overlaps(scale_shards[r], sb, full, full_bytes))
@@ -361,7 +401,7 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards, c
     for (int u = unit_begin; u < unit_end; ++u) {
         const UnitInfo& ui = plan->units[u];
         if (ui.slice_numel == 0) continue;
-        const dim3 grid(unsigned(ceil_div(ui.slice_numel / 4, kDeqTileQuads)), unsigned(owners));
+        const dim3 grid(unsigned(ceil_div(ui.slice_numel / 8, kGDTileOcts)), unsigned(owners));
         hipError_t e;
         if (dtype == ZERO_F16)
             e = bits == 8 ? launch_gather_dequant<ZERO_F16, 8>(device_table, grid, s, ct, st, dct, dst, ui.slice_numel,

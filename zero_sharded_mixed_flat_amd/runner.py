@@ -9,6 +9,12 @@ the ABI requires), fills them from the seeded generators, and runs steps:
     AdamW + 16-bit cast into the parameter buffer zero_adam_step      (a3)
     per-unit gather of every rank's 16-bit shard  zero_gather_params  (a4)
 
+With a block-quantised gather (ZeRO++ quantised weights) the last step is
+
+    quantise the rank's updated 16-bit shard      zero_quantize_blocks
+    per-unit gather of every rank's codes,
+    dequantised into the 16-bit full buffer       zero_gather_dequant
+
 All calls go to one stream with no host synchronisation inside a step: the
 clip multiplier and the skip flag stay in device memory.  Contributions of the
 emulated ranks are buffers in this GPU's memory (one process, one GPU).
@@ -94,6 +100,18 @@ class RankStep:
         else:
             self.full = torch.zeros(self.full_numel, dtype=pdt, device=dev)
 
+        # Block-quantised gather: codes and scales as every rank would send
+        # them; the other ranks' come from quantising their synthetic 16-bit
+        # shards once.
+        self.codes = self.scales = None
+        if w.gather_bits != 16:
+            cb = abi.zero_quant_code_bytes(n, w.gather_bits)
+            self.codes = torch.empty((w.nd, cb), dtype=torch.uint8, device=dev)
+            self.scales = torch.empty((w.nd, abi.zero_quant_scale_count(n)), dtype=torch.float32, device=dev)
+            for r in range(w.nd):
+                if r not in self.owners:
+                    self.quantize_shard(r)
+
         n_sets = 1 if w.pre_reduced else len(self.owners)
         self.ws = torch.empty(abi.zero_workspace_bytes(n, n_sets), dtype=torch.uint8, device=dev)
         self.n_sets = n_sets
@@ -165,9 +183,21 @@ class RankStep:
             abi.zero_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype, self.n,
                                hp, self.coef, self.flag, self.param_out(i), w.param_dtype, stream)
 
+    def quantize_shard(self, r, stream=None):
+        abi.zero_quantize_blocks(self.shards[r], self.w.param_dtype, self.n, self.w.gather_bits, self.codes[r],
+                                 self.scales[r], stream)
+
+    def quantize_all(self, stream=None):
+        for o in self.owners:
+            self.quantize_shard(o, stream)
+
     def gather_unit(self, u, stream=None):
-        abi.zero_gather_params(self.plan, list(self.shards), u, u + 1, self.w.param_dtype, self.full,
-                               self.ws, stream)
+        if self.codes is not None:
+            abi.zero_gather_dequant(self.plan, list(self.codes), list(self.scales), u, u + 1, self.w.gather_bits,
+                                    self.w.param_dtype, self.full, self.ws, stream)
+        else:
+            abi.zero_gather_params(self.plan, list(self.shards), u, u + 1, self.w.param_dtype, self.full,
+                                   self.ws, stream)
 
     def gather_all(self, stream=None):
         for u in range(self.n_units):
@@ -180,6 +210,8 @@ class RankStep:
             self.reduce_all(stream)
         self.norm_all(stream)
         self.adam_all(stream)
+        if self.codes is not None:
+            self.quantize_all(stream)
         if self.shards is not None:
             self.gather_all(stream)
         self.t += 1
@@ -193,11 +225,18 @@ class RankStep:
         reduced) + 24 (read and write master, m, v) + 2 (write the 16-bit
         parameter); 30 bytes when the gradient arrives reduced (2 to read it for
         the norm, 2 to read it again in Adam, ...).  A ZeRO-3 gather adds 4
-        bytes (read + write) per gathered element.
+        bytes (read + write) per gathered element.  A block-quantised gather
+        instead reads the 16-bit shard and writes its codes and scales once per
+        owned element (2 + b/8 + 4/256), then reads codes and scales and writes
+        16 bits per gathered element (b/8 + 4/256 + 2).
         """
         w = self.w
         per = 30 if w.pre_reduced else 2 * w.nd + 30
         total = per * self.n * len(self.owners)
-        if self.shards is not None:
+        if self.codes is not None:
+            code = self.codes.shape[1] + 4 * self.scales.shape[1]     # bytes of one rank's codes + scales
+            total += (2 * self.n + code) * len(self.owners)
+            total += (code + 2 * self.n) * w.nd
+        elif self.shards is not None:
             total += 4 * self.n * w.nd
         return total

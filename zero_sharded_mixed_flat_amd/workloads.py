@@ -16,6 +16,12 @@ Shapes follow the pages' examples:
   bucket on 16 ranks under ZeRO-1, fp16 with a loss scale of 65536.
 * ``gpt3_175b_nd16_z1``: a 175e9-parameter vector (GPT-3 175B sized, Lecture 18
   notes §1.2) on 16 ranks; the rank's owner update on a pre-reduced gradient.
+* ``paper_7p5b_nd64_z3_qwz8`` / ``_qwz4``: the ZeRO-3 workload with the
+  ZeRO++ quantised-weight gather (Lecture 18 notes §4.5): the rank quantises
+  its updated 16-bit shard to INT8 / INT4 codes with one scale per 256
+  elements, and every unit is gathered from all ranks' codes, dequantised
+  into the 16-bit full buffer.  Slices are aligned to 256 so a block never
+  straddles two owners.
 """
 
 from dataclasses import dataclass, field
@@ -48,6 +54,7 @@ class Workload:
     pre_reduced: bool = False     # the gradient arrives already averaged (owner update only)
     gather_per_unit: bool = False # the 16-bit shards of every rank are gathered unit by unit
     gather_shard_std: float = 0.0 # other ranks' 16-bit parameter shards ~ N(0, this)
+    gather_bits: int = 16         # 16: plain gather; 8 or 4: block-quantised codes
     steps: int = 1
     align: int = 8
     tensors: tuple = field(default=None, repr=False)   # ragged tensor sizes, if any
@@ -95,6 +102,15 @@ WORKLOADS = {
             master_std=0.02, m_std=0.0, v_std=0.0,
             lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_norm=1.0,
             rank=0, gather_per_unit=True, gather_shard_std=0.02),
+        *[Workload(
+            name=f"paper_7p5b_nd64_z3_qwz{bits}", psi=7_500_000_000, nd=64, stage=3,
+            units=(156_250_000,) * 48,
+            grad_dtype="f16", param_dtype="f16", grad_std=1e-3,
+            outlier_frac=0.01, outlier_mult=100.0,
+            master_std=0.02, m_std=0.0, v_std=0.0,
+            lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_norm=1.0,
+            rank=0, gather_per_unit=True, gather_shard_std=0.02, gather_bits=bits, align=256)
+          for bits in (8, 4)],
         Workload(
             name="gpt2_1p5b_nd16_z1", psi=sum(_GPT2), nd=16, stage=1, units=(sum(_GPT2),),
             grad_dtype="f16", param_dtype="f16", grad_std=1e-3, loss_scale=65536.0,
