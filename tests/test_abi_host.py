@@ -234,3 +234,19 @@ def test_gather_dequant_rejects():
     with pytest.raises(abi.ZeroError) as e:
         abi.zero_gather_dequant(plan, [A, A + 8, A, A], [W] * 4, 0, 2, 8, 1, B, stream=0)   # codes not 16-aligned
     assert e.value.code == abi.ZERO_EINVAL and "shard 1" in str(e.value)
+
+
+def test_pointer_table():
+    import torch
+    plan = abi.Plan([4096, 2048], 4, 3, 256)
+    codes = abi.PointerTable([A, A + 16, A + 32, A + 48], 1 << 20)    # raw addresses are not size-checked
+    scales = abi.PointerTable([W] * 4, 1 << 20)
+    assert len(codes) == 4 and list(codes.array) == [A, A + 16, A + 32, A + 48]
+    with pytest.raises(abi.ZeroError) as e:        # the table reaches the library's own checks
+        abi.zero_gather_dequant(plan, codes, scales, 0, 2, 8, 1, B + 8, stream=0)
+    assert "16-byte" in str(e.value)
+    small = abi.PointerTable([torch.empty(0)] * 4, 0)
+    with pytest.raises(ValueError):                # validated for fewer bytes than the call needs
+        abi.zero_gather_params(plan, small, 0, 2, "f16", None, stream=0)
+    with pytest.raises(ValueError):                # host tensors are refused when the table is built
+        abi.PointerTable([torch.empty(8)], 32, "shard")

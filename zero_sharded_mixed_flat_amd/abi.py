@@ -161,6 +161,39 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+class PointerTable:
+    """A host array of device pointers to a list of tensors, marshalled once.
+
+    Entry points that take one buffer per rank accept a table in place of the
+    list, which saves re-marshalling (and re-validating) the same pointers on
+    every call.  The table keeps references to its tensors, so their memory
+    stays valid while it lives.  Every tensor is checked against ``nbytes``
+    (a contiguous device tensor holding at least that many bytes) when the
+    table is built.
+    """
+
+    def __init__(self, tensors, nbytes, what="buffer"):
+        self.tensors = list(tensors)
+        for i, t in enumerate(self.tensors):
+            _need(t, nbytes, f"{what} {i}")
+        self.nbytes = int(nbytes)
+        self.array = (_P * len(self.tensors))(*[_ptr(t) for t in self.tensors])
+
+    def __len__(self):
+        return len(self.tensors)
+
+
+def _table(buffers, nbytes, what):
+    """Pointer array for a list of tensors (validated) or a prebuilt PointerTable."""
+    if isinstance(buffers, PointerTable):
+        if buffers.nbytes < nbytes:
+            raise ValueError(f"{what} table was validated for {buffers.nbytes} bytes per buffer, needs {nbytes}")
+        return buffers.array
+    for i, t in enumerate(buffers):
+        _need(t, nbytes, f"{what} {i}")
+    return (_P * len(buffers))(*[_ptr(t) for t in buffers])
+
+
 # ---------------------------------------------------------------------------
 # a0: partition
 # ---------------------------------------------------------------------------
@@ -175,6 +208,7 @@ class Plan:
         _check(lib.zero_plan_create(sizes, len(unit_numels), int(nd), int(stage), int(align),
                                     ctypes.byref(handle)))
         self.handle = handle
+        self._cache = {}
 
     def close(self):
         if self.handle:
@@ -185,15 +219,20 @@ class Plan:
         self.close()
 
     def info(self):
-        a, b, c, d = _I(), _I(), _I(), _I()
-        _check(lib.zero_plan_info(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
-                                  ctypes.byref(d)))
-        return {"n_units": a.value, "owners": b.value, "nd": c.value, "stage": d.value}
+        if "info" not in self._cache:
+            a, b, c, d = _I(), _I(), _I(), _I()
+            _check(lib.zero_plan_info(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                      ctypes.byref(d)))
+            self._cache["info"] = {"n_units": a.value, "owners": b.value, "nd": c.value, "stage": d.value}
+        return dict(self._cache["info"])
 
     def rank(self, rank):
-        s, r = _I64(), _I64()
-        _check(lib.zero_plan_rank(self.handle, int(rank), ctypes.byref(s), ctypes.byref(r)))
-        return s.value, r.value
+        key = ("rank", int(rank))
+        if key not in self._cache:
+            s, r = _I64(), _I64()
+            _check(lib.zero_plan_rank(self.handle, int(rank), ctypes.byref(s), ctypes.byref(r)))
+            self._cache[key] = (s.value, r.value)
+        return self._cache[key]
 
     def unit(self, unit):
         a, b, c, d = _I64(), _I64(), _I64(), _I64()
@@ -202,9 +241,11 @@ class Plan:
         return a.value, b.value, c.value, d.value
 
     def full_numel(self):
-        x = _I64()
-        _check(lib.zero_plan_full_numel(self.handle, ctypes.byref(x)))
-        return x.value
+        if "full" not in self._cache:
+            x = _I64()
+            _check(lib.zero_plan_full_numel(self.handle, ctypes.byref(x)))
+            self._cache["full"] = x.value
+        return self._cache["full"]
 
     def segments(self, tensor_numels, rank):
         sizes = (_I64 * len(tensor_numels))(*[int(t) for t in tensor_numels])
@@ -250,11 +291,9 @@ def zero_workspace_bytes(n, n_sets):
 
 def zero_reduce_shard(contribs, n, dtype, inv_loss_scale, reduced_out, workspace, set_index, flag,
                       stream=None, workspace_bytes=None):
-    for i, c in enumerate(contribs):
-        _need(c, 2 * n, f"contribution {i}")
+    ptrs = _table(contribs, 2 * n, "contribution")
     _need(reduced_out, 2 * n, "reduced_out")
     _need(flag, 4, "flag")
-    ptrs = (_P * len(contribs))(*[_ptr(c) for c in contribs])
     wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     _check(lib.zero_reduce_shard(ptrs, len(contribs), int(n), _dtype(dtype), float(inv_loss_scale),
                                  _ptr(reduced_out), _ptr(workspace), wb, int(set_index), _ptr(flag),
@@ -291,7 +330,6 @@ def zero_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, flag, param_out,
 
 def zero_gather_params(plan, shards, unit_begin, unit_end, dtype, full, workspace=None, stream=None,
                        workspace_bytes=None):
-    ptrs = (_P * len(shards))(*[_ptr(s) for s in shards])
     wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     handle = plan.handle if isinstance(plan, Plan) else plan
     if isinstance(plan, Plan):
@@ -299,9 +337,10 @@ def zero_gather_params(plan, shards, unit_begin, unit_end, dtype, full, workspac
         if len(shards) != info["owners"]:
             raise ValueError(f"need {info['owners']} shards, got {len(shards)}")
         shard_numel, _ = plan.rank(0)
-        for i, sh in enumerate(shards):
-            _need(sh, 2 * shard_numel, f"shard {i}")
+        ptrs = _table(shards, 2 * shard_numel, "shard")
         _need(full, 2 * plan.full_numel(), "full")
+    else:
+        ptrs = _table(shards, 0, "shard")
     _check(lib.zero_gather_params(handle, ptrs, int(unit_begin), int(unit_end), _dtype(dtype),
                                   _ptr(full), _ptr(workspace), wb, _stream(stream)))
 
@@ -344,19 +383,19 @@ def zero_dequantize_blocks(codes, scales, n, bits, y, dtype, stream=None):
 
 def zero_gather_dequant(plan, code_shards, scale_shards, unit_begin, unit_end, bits, dtype, full, workspace=None,
                         stream=None, workspace_bytes=None):
-    cp = (_P * len(code_shards))(*[_ptr(c) for c in code_shards])
-    sp = (_P * len(scale_shards))(*[_ptr(c) for c in scale_shards])
     wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     handle = plan.handle if isinstance(plan, Plan) else plan
+    code_bytes = scale_bytes = 0
     if isinstance(plan, Plan):
         owners = plan.info()["owners"]
         if len(code_shards) != owners or len(scale_shards) != owners:
             raise ValueError(f"need {owners} code and scale shards")
         shard_numel, _ = plan.rank(0)
         if bits in (8, 4):
-            for i in range(owners):
-                _need(code_shards[i], zero_quant_code_bytes(shard_numel, bits), f"code shard {i}")
-                _need(scale_shards[i], 4 * zero_quant_scale_count(shard_numel), f"scale shard {i}")
+            code_bytes = zero_quant_code_bytes(shard_numel, bits)
+            scale_bytes = 4 * zero_quant_scale_count(shard_numel)
         _need(full, 2 * plan.full_numel(), "full")
+    cp = _table(code_shards, code_bytes, "code shard")
+    sp = _table(scale_shards, scale_bytes, "scale shard")
     _check(lib.zero_gather_dequant(handle, cp, sp, int(unit_begin), int(unit_end), int(bits), _dtype(dtype),
                                    _ptr(full), _ptr(workspace), wb, _stream(stream)))

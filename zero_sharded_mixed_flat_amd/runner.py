@@ -112,6 +112,15 @@ class RankStep:
                 if r not in self.owners:
                     self.quantize_shard(r)
 
+        # Per-rank pointer lists, marshalled once (the buffers never move).
+        self.contrib_tables = None if w.pre_reduced else [
+            abi.PointerTable(self.contribs(i), 2 * n, "contribution") for i in range(len(self.owners))]
+        self.shard_table = None if self.shards is None else abi.PointerTable(list(self.shards), 2 * n, "shard")
+        self.code_table = self.scale_table = None
+        if self.codes is not None:
+            self.code_table = abi.PointerTable(list(self.codes), self.codes.shape[1], "code shard")
+            self.scale_table = abi.PointerTable(list(self.scales), 4 * self.scales.shape[1], "scale shard")
+
         n_sets = 1 if w.pre_reduced else len(self.owners)
         self.ws = torch.empty(abi.zero_workspace_bytes(n, n_sets), dtype=torch.uint8, device=dev)
         self.n_sets = n_sets
@@ -167,7 +176,7 @@ class RankStep:
 
     def reduce_all(self, stream=None):
         for i in range(len(self.owners)):
-            abi.zero_reduce_shard(self.contribs(i), self.n, self.w.grad_dtype, self.w.inv_loss_scale,
+            abi.zero_reduce_shard(self.contrib_tables[i], self.n, self.w.grad_dtype, self.w.inv_loss_scale,
                                   self.reduced[i], self.ws, i, self.flag, stream)
 
     def norm_all(self, stream=None):
@@ -193,10 +202,10 @@ class RankStep:
 
     def gather_unit(self, u, stream=None):
         if self.codes is not None:
-            abi.zero_gather_dequant(self.plan, list(self.codes), list(self.scales), u, u + 1, self.w.gather_bits,
+            abi.zero_gather_dequant(self.plan, self.code_table, self.scale_table, u, u + 1, self.w.gather_bits,
                                     self.w.param_dtype, self.full, self.ws, stream)
         else:
-            abi.zero_gather_params(self.plan, list(self.shards), u, u + 1, self.w.param_dtype, self.full,
+            abi.zero_gather_params(self.plan, self.shard_table, u, u + 1, self.w.param_dtype, self.full,
                                    self.ws, stream)
 
     def gather_all(self, stream=None):
