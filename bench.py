@@ -8,8 +8,9 @@ plain or block-quantised).
 
 Prints ONE JSON line.  ``value`` is parameters updated per second by this GPU
 (the whole job at one GPU).  ``roofline`` reports the dominant kernel (the
-AdamW kernel: 28 algorithmic bytes per element) against MI355X's 8 TB/s HBM,
-timed with HIP events on the stream the kernels run on.  ``cpu_baseline`` is
+phase with the longest time per step: AdamW at 28 algorithmic bytes per
+element on the default workload) against MI355X's 8 TB/s HBM, timed with HIP
+events on the stream the kernels run on.  ``cpu_baseline`` is
 the CPU oracle timed on a bounded sample of the same workload's inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -28,7 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "zero_sharded_mixed_flat_amd", "csrc", f)
-                  for f in ("kernels.hip", "internal.h")]
+                  for f in ("kernels.hip", "quant.hip", "device.h", "internal.h")]
 COPY_ELEMS = 1 << 31            # the reference copy: 4 GiB of 16-bit values
 COPY_BYTES_EACH_WAY = 2 * COPY_ELEMS
 
@@ -45,10 +46,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters.
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of one kernel of a workload from committed rocprofv3 counters.
 
-    Only used when the counters were taken from the current kernel source.
+    Only used when the counters were taken from the current kernel sources.
     """
     try:
         with open(TRAFFIC_FILE) as f:
@@ -58,7 +59,7 @@ def measured_traffic(workload):
     entry = data.get(workload)
     if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return entry.get("bytes_per_launch")
+    return entry.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
 def cpu_baseline(run, budget_s=12.0):
@@ -147,12 +148,13 @@ def summarize_trace(stats_csv, command):
     return "\n".join(out) + "\n"
 
 
-def summarize_counters(fetch_csv, write_csv, workload, alg_bytes, commands):
+def summarize_counters(fetch_csv, write_csv, phases, commands):
     """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, scaled by the reference copy.
 
     The reference copy is the 4 GiB -> 4 GiB gather dispatch in the same run;
-    its known byte counts give one scale factor per counter.  Returns the
-    markdown summary and the traffic entry for the dominant (AdamW) kernel.
+    its known byte counts give one scale factor per counter.  ``phases`` is the
+    workload's phase model (kernel, launches, algorithmic bytes per launch).
+    Returns the markdown summary and the traffic entry of every phase kernel.
     """
     import csv
     from collections import defaultdict
@@ -163,35 +165,40 @@ def summarize_counters(fetch_csv, write_csv, workload, alg_bytes, commands):
             if r["Counter_Name"] != counter or "zf::" not in r["Kernel_Name"]:
                 continue
             acc[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
-        per[counter] = {k: sum(v) / len(v) for k, v in acc.items()}
+        per[counter] = {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
     copy_grid = COPY_ELEMS // 8 // 2    # 16-byte pieces, two per lane: one lane per 16 elements
     copy_key = [k for k in per["FETCH_SIZE"] if k[0].startswith("gather_kernel") and k[1] == copy_grid]
     if not copy_key:
         raise RuntimeError("no reference copy dispatch in the counter files")
     ck = copy_key[0]
     ref_kib = COPY_BYTES_EACH_WAY / 1024
-    fetch_scale = ref_kib / per["FETCH_SIZE"][ck]
-    write_scale = ref_kib / per["WRITE_SIZE"][ck]
+    fetch_scale = ref_kib / per["FETCH_SIZE"][ck][0]
+    write_scale = ref_kib / per["WRITE_SIZE"][ck][0]
     out = ["# HBM byte counters", "", "Commands:", "", "```"] + list(commands) + ["```", "",
            f"Reference: the gather kernel copying {COPY_BYTES_EACH_WAY} bytes to another buffer "
-           f"(grid {ck[1]}) read FETCH_SIZE {per['FETCH_SIZE'][ck]:.6g} KiB and WRITE_SIZE "
-           f"{per['WRITE_SIZE'][ck]:.6g} KiB per dispatch, so the scale factors are "
+           f"(grid {ck[1]}) read FETCH_SIZE {per['FETCH_SIZE'][ck][0]:.6g} KiB and WRITE_SIZE "
+           f"{per['WRITE_SIZE'][ck][0]:.6g} KiB per dispatch, so the scale factors are "
            f"{fetch_scale:.5f} (fetch) and {write_scale:.5f} (write).", "",
-           "| kernel | grid | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes read | scaled bytes written | scaled total |",
-           "|---|---|---|---|---|---|---|"]
-    entry = None
-    for k in sorted(per["FETCH_SIZE"], key=lambda k: -per["FETCH_SIZE"][k]):
-        f = per["FETCH_SIZE"][k]
-        w = per["WRITE_SIZE"].get(k, float("nan"))
+           "| kernel | grid | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes read "
+           "| scaled bytes written | scaled total | algorithmic | ratio |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    by_prefix = {p["kernel"]: p for p in phases.values()}
+    kernels = {}
+    for k in sorted(per["FETCH_SIZE"], key=lambda k: -per["FETCH_SIZE"][k][0]):
+        f, count = per["FETCH_SIZE"][k]
+        w = per["WRITE_SIZE"].get(k, (float("nan"), 0))[0]
         rb, wb = f * 1024 * fetch_scale, w * 1024 * write_scale
-        out.append(f"| `{k[0]}` | {k[1]} | {f:.6g} | {w:.6g} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} |")
-        if k[0].startswith("adam_kernel"):
-            entry = {"kernel": k[0], "bytes_per_launch": rb + wb, "bytes_read": rb, "bytes_written": wb,
-                     "algorithmic_bytes_per_launch": alg_bytes, "fetch_scale": fetch_scale,
-                     "write_scale": write_scale, "kernel_source_sha256_16": kernel_source_hash()}
-    if entry:
-        out += ["", f"AdamW: {entry['bytes_per_launch']:.5g} bytes per launch against "
-                f"{alg_bytes:.5g} algorithmic bytes ({entry['bytes_per_launch'] / alg_bytes:.4f}x)."]
+        prefix = k[0].split("<")[0]
+        phase = by_prefix.get(prefix) if k != ck else None
+        alg = phase["bytes_per_launch"] if phase else None
+        ratio = f"{(rb + wb) / alg:.4f}x" if alg else ""
+        out.append(f"| `{k[0]}` | {k[1]} | {count} | {f:.6g} | {w:.6g} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} "
+                   f"| {alg if alg is None else f'{alg:.4g}'} | {ratio} |")
+        if phase and prefix not in kernels:
+            kernels[prefix] = {"kernel": k[0], "grid": k[1], "bytes_per_launch": rb + wb, "bytes_read": rb,
+                               "bytes_written": wb, "algorithmic_bytes_per_launch": alg}
+    entry = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_scale": fetch_scale,
+             "write_scale": write_scale, "kernels": kernels}
     return "\n".join(out) + "\n", entry
 
 
@@ -215,13 +222,13 @@ def main():
         print(summarize_trace(args.summarize_trace, "\n".join(args.command)), end="")
         return 0
     if args.summarize_counters:
+        from zero_sharded_mixed_flat_amd import abi as _abi
+        from zero_sharded_mixed_flat_amd import runner as _runner
         from zero_sharded_mixed_flat_amd import workloads as _wl
         name = args.workload or _wl.BENCH_DEFAULT
         w = _wl.get(name)
-        from zero_sharded_mixed_flat_amd import abi as _abi
-        n, _ = _abi.Plan(w.units, w.nd, w.stage, w.align).rank(0)
-        owners = w.nd if w.all_ranks else 1
-        text, entry = summarize_counters(*args.summarize_counters, name, 28 * n * owners, args.command)
+        phases = _runner.phase_model(w, _abi.Plan(w.units, w.nd, w.stage, w.align))
+        text, entry = summarize_counters(*args.summarize_counters, phases, args.command)
         print(text, end="")
         if entry:
             try:
@@ -326,11 +333,17 @@ def main():
 
     owned = run.n * len(run.owners)
     alg_bytes = run.algorithmic_bytes()
-    adam_bytes = 28 * owned
-    adam_gbs = adam_bytes / (kern_ms["adam"] * 1e-3) / 1e9
     step_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     flag = int(run.flag.item())
-    traffic = measured_traffic(name)
+    # The dominant kernel: the phase with the longest time per step.  Its
+    # launches are timed together, so the per-launch time is the phase time
+    # over its launch count (gaps between launches included).
+    phase_model = run.phases()
+    dom = max(phase_model, key=lambda p: kern_ms[p])
+    dom_launch_ms = kern_ms[dom] / phase_model[dom]["launches"]
+    dom_bytes = phase_model[dom]["bytes_per_launch"]
+    dom_gbs = dom_bytes / (dom_launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic(name, phase_model[dom]["kernel"])
 
     result = {
         "metric": "sharded Adam step: params updated/s and achieved HBM GB/s (% of peak), 1 GPU",
@@ -357,16 +370,18 @@ def main():
         "copy_ceiling": {"kernel": "gather_kernel as a plain 4 GiB -> 4 GiB copy", "gbs": copy_gbs,
                          "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
                          "step_frac_of_copy": step_gbs / copy_gbs,
-                         "adam_frac_of_copy": adam_gbs / copy_gbs},
+                         "dominant_frac_of_copy": dom_gbs / copy_gbs},
         "roofline": {
             "bound": "hbm",
-            "kernel": "adam_kernel",
-            "achieved": adam_gbs,
+            "kernel": phase_model[dom]["kernel"],
+            "achieved": dom_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": adam_gbs / HBM_PEAK_GBS,
+            "frac": dom_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": adam_bytes,
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "launch_ms": dom_launch_ms,
+            "launches_per_step": phase_model[dom]["launches"],
         },
         "step_flag": flag,
         "norm": float(run.norm.item()),

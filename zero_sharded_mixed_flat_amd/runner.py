@@ -227,25 +227,40 @@ class RankStep:
 
     # -- accounting ------------------------------------------------------------
 
-    def algorithmic_bytes(self):
-        """Bytes the step must move per the method (not counting re-reads).
+    def phases(self):
+        return phase_model(self.w, self.plan)
 
-        Per owned element: 2*Nd (contributions) + 2 (write reduced) + 2 (read
-        reduced) + 24 (read and write master, m, v) + 2 (write the 16-bit
-        parameter); 30 bytes when the gradient arrives reduced (2 to read it for
-        the norm, 2 to read it again in Adam, ...).  A ZeRO-3 gather adds 4
-        bytes (read + write) per gathered element.  A block-quantised gather
-        instead reads the 16-bit shard and writes its codes and scales once per
-        owned element (2 + b/8 + 4/256), then reads codes and scales and writes
-        16 bits per gathered element (b/8 + 4/256 + 2).
-        """
-        w = self.w
-        per = 30 if w.pre_reduced else 2 * w.nd + 30
-        total = per * self.n * len(self.owners)
-        if self.codes is not None:
-            code = self.codes.shape[1] + 4 * self.scales.shape[1]     # bytes of one rank's codes + scales
-            total += (2 * self.n + code) * len(self.owners)
-            total += (code + 2 * self.n) * w.nd
-        elif self.shards is not None:
-            total += 4 * self.n * w.nd
-        return total
+    def algorithmic_bytes(self):
+        return sum(p["launches"] * p["bytes_per_launch"] for p in self.phases().values())
+
+
+def phase_model(w, plan):
+    """Kernel, launches per step and algorithmic bytes per launch of each phase.
+
+    Algorithmic bytes are what the method must move, not counting re-reads.
+    Per owned element: the reduce reads 2*Nd bytes of contributions and
+    writes the 2-byte reduced gradient; AdamW reads it (2), reads and writes
+    master, m and v (24) and writes the 16-bit parameter (2).  A gradient that
+    arrives reduced is read once more by the norm pass (2).  A ZeRO-3 gather
+    reads and writes 2 bytes per gathered element.  A block-quantised gather
+    instead reads the 16-bit shard and writes its codes and scales once per
+    owned element (2 + b/8 + 4/256), then reads codes and scales and writes 16
+    bits per gathered element (b/8 + 4/256 + 2).  Needs no GPU.
+    """
+    n, _ = plan.rank(0)
+    n_units = plan.info()["n_units"]
+    owners = w.nd if w.all_ranks else 1
+    out = {}
+    if not w.pre_reduced:
+        out["reduce"] = {"kernel": "reduce_kernel", "launches": owners, "bytes_per_launch": (2 * w.nd + 2) * n}
+    out["norm"] = {"kernel": "sumsq_kernel" if w.pre_reduced else "finalize_kernel", "launches": 1,
+                   "bytes_per_launch": 2 * n if w.pre_reduced else 0}
+    out["adam"] = {"kernel": "adam_kernel", "launches": owners, "bytes_per_launch": 28 * n}
+    if w.gather_bits != 16:
+        code = abi.zero_quant_code_bytes(n, w.gather_bits) + 4 * abi.zero_quant_scale_count(n)
+        out["quantize"] = {"kernel": "quantize_kernel", "launches": owners, "bytes_per_launch": 2 * n + code}
+        out["gather"] = {"kernel": "gather_dequant_kernel", "launches": n_units,
+                         "bytes_per_launch": (code + 2 * n) * w.nd / n_units}
+    elif w.gather_per_unit:
+        out["gather"] = {"kernel": "gather_kernel", "launches": n_units, "bytes_per_launch": 4 * n * w.nd / n_units}
+    return out
