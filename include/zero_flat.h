@@ -326,6 +326,67 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards,
                         void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* CPU-offloaded optimizer (ZeRO-Offload)                                  */
+/* ---------------------------------------------------------------------- */
+
+/* Instruction sets of the host AdamW (zero_cpu_isa / zero_cpu_set_isa). */
+#define ZERO_CPU_SCALAR 0
+#define ZERO_CPU_AVX2 1   /* AVX2 + F16C, 8 values per instruction */
+#define ZERO_CPU_AVX512 2 /* AVX-512 F/BW/VL + F16C, 16 values per instruction */
+
+/* Minimum size of the pinned staging buffer of zero_offload_adam_step. */
+#define ZERO_OFFLOAD_MIN_STAGING 576
+
+/*
+ * zero_cpu_adam_step -- the AdamW update of zero_adam_step on HOST memory, for
+ * ZeRO-Offload, which keeps the fp32 master, m and v (12 bytes per parameter)
+ * in host memory and updates them with a multi-threaded, vectorised CPU Adam
+ * (L18 notes §4.4).  Same formula and the same fp32 operation sequence as the
+ * GPU kernel (no fused multiply-add), with g = f32(grad) * inv_loss_scale *
+ * coef; the result does not depend on n_threads or on the instruction set.
+ *
+ * master, m, v: host fp32, n each, distinct, 4-byte aligned.  grad: host
+ * 16-bit (`grad_dtype`), n.  param_out: host 16-bit (`param_dtype`), n.  coef:
+ * the clip multiplier (finite, > 0).  skip != 0 writes nothing (a non-finite
+ * gradient).  n_threads in [1, 256]: the range is cut into that many
+ * contiguous parts (fewer for small n); the call returns when all are done.
+ */
+int zero_cpu_adam_step(float* master, float* m, float* v, const void* grad, int grad_dtype,
+                       int64_t n, const zero_adam_hparams* hp, float coef, int skip,
+                       void* param_out, int param_dtype, int n_threads);
+
+/*
+ * zero_offload_adam_step -- one ZeRO-Offload update of an owned slice: the
+ * reduced 16-bit gradient goes from the GPU to the host, the host AdamW
+ * updates the host fp32 state, and the 16-bit parameters go back (2 bytes
+ * each way per parameter; L18 notes §4.4).  The work is cut into chunks that
+ * fit the staging buffer; the copy of the next chunk's gradient overlaps the
+ * update of the current one, and its parameters are copied back while the
+ * next chunk is updated.  The clip multiplier and the skip flag are read
+ * from the device first (zero_grad_norm's outputs); a set flag moves nothing.
+ *
+ * master, m, v: host fp32, n each.  grad_dev: device 16-bit, n.  coef_dev,
+ * flag_dev: device fp32 / int32.  param_dev: device 16-bit, n.  staging:
+ * host memory allocated pinned (hipHostMalloc), 64-byte aligned, at least
+ * ZERO_OFFLOAD_MIN_STAGING bytes; (staging_bytes - 64) / 8 values per chunk.
+ * Blocks the calling thread until the last parameters have reached the
+ * device (the stream is synchronised).  Errors: ZERO_EINVAL (arguments, or a
+ * non-positive clip multiplier on the device), ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_dev,
+                           int grad_dtype, int64_t n, const zero_adam_hparams* hp,
+                           const float* coef_dev, const int32_t* flag_dev, void* param_dev,
+                           int param_dtype, void* staging, int64_t staging_bytes, int n_threads,
+                           void* stream);
+
+/* The host AdamW's instruction set in use (ZERO_CPU_*). */
+int zero_cpu_isa(void);
+
+/* Use a lower instruction set than detected (for tests); EINVAL if the CPU
+ * lacks it. */
+int zero_cpu_set_isa(int isa);
+
+/* ---------------------------------------------------------------------- */
 /* Misc                                                                    */
 /* ---------------------------------------------------------------------- */
 

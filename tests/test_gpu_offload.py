@@ -1,0 +1,114 @@
+"""GPU parity of the ZeRO-Offload update (``zero_offload_adam_step``).
+
+The reduced gradient and the clip multiplier live on the GPU, the fp32 state
+in host memory; the host state and the 16-bit parameters that come back to
+the device are compared with the oracle's AdamW, and bit for bit with the host
+AdamW called directly on the same inputs (the chunking and the overlap of
+copies with the update change nothing).  Staging buffers down to the minimum
+force many chunks and a ragged last one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rounding, step
+from oracle.step import AdamHparams
+from zero_sharded_mixed_flat_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TORCH16 = synth.TORCH_DTYPES
+HP = AdamHparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, inv_loss_scale=2.0 ** -4)
+
+
+@pytest.fixture(scope="module")
+def abi():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from zero_sharded_mixed_flat_amd import abi as _abi
+    return _abi
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def _abi_hp(abi, hp, t):
+    return abi.adam_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.inv_loss_scale, t)
+
+
+def _inputs(n, gdt, seed):
+    rng = np.random.default_rng(seed)
+    g = rounding.narrow((rng.standard_normal(n) * 1e-3 / HP.inv_loss_scale).astype(np.float32), gdt)
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32)
+    return g, p, m, v
+
+
+def _state_ok(got, ref, what):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    bad = np.flatnonzero(np.abs(got - ref) > 1e-9 + 1e-6 * np.abs(ref))
+    assert bad.size == 0, f"{what}: {bad.size} out of tolerance"
+
+
+def _ulp_ok(got, ref, what):
+    d = np.abs(rounding.ordered16(got) - rounding.ordered16(ref))
+    assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} values more than 1 ulp apart"
+
+
+def _offload(abi, g, p, m, v, gdt, pdt, t, coef, flag, staging_bytes, threads=4, declared=None):
+    n = g.size
+    hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
+    dg = torch.from_numpy(g.view(np.int16).copy()).cuda()
+    dp = torch.full((n,), 7, dtype=torch.int16, device="cuda")
+    dcoef = torch.tensor([coef], dtype=torch.float32, device="cuda")
+    dflag = torch.tensor([flag], dtype=torch.int32, device="cuda")
+    staging = torch.empty(staging_bytes, dtype=torch.uint8, pin_memory=True)
+    abi.zero_offload_adam_step(hm, hmm, hv, dg, gdt, n, _abi_hp(abi, HP, t), dcoef, dflag, dp, pdt, staging,
+                               threads, staging_bytes=declared)
+    return hm.numpy(), hmm.numpy(), hv.numpy(), dp.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("gdt, pdt", [("bf16", "bf16"), ("f16", "f16"), ("f16", "bf16")])
+@pytest.mark.parametrize("n", [1, 63, 64, 1000, 100_003])
+@pytest.mark.parametrize("staging", [576, 64 + 8 * 4096, 64 + 8 * (1 << 20)])
+def test_offload_matches_oracle_and_host_adam(abi, gdt, pdt, n, staging):
+    _note(f"offload n={n} staging={staging} {gdt}->{pdt}")
+    g, p, m, v = _inputs(n, gdt, n + staging)
+    coef = np.float32(0.6)
+    got = _offload(abi, g, p, m, v, gdt, pdt, 3, float(coef), 0, staging)
+    ref = step.adam_update(p, m, v, g, gdt, HP, 3, coef, pdt)
+    for k, what in enumerate(("master", "m", "v")):
+        _state_ok(got[k], ref[k], what)
+    _ulp_ok(got[3], ref[3], "param")
+    # the same update by the host AdamW called directly: identical bits
+    hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
+    out = torch.zeros(n, dtype=torch.int16)
+    abi.zero_cpu_adam_step(hm, hmm, hv, torch.from_numpy(g.view(np.int16).copy()), gdt, n, _abi_hp(abi, HP, 3),
+                           float(coef), False, out, pdt, 2)
+    for a, b in zip(got, (hm.numpy(), hmm.numpy(), hv.numpy(), out.numpy().view(np.uint16))):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
+def test_offload_skip_moves_nothing(abi):
+    g, p, m, v = _inputs(5000, "bf16", 1)
+    got = _offload(abi, g, p, m, v, "bf16", "bf16", 1, 1.0, 1, 64 + 8 * 1024)
+    assert np.array_equal(got[0], p) and np.array_equal(got[1], m) and np.array_equal(got[2], v)
+    assert np.all(got[3] == 7)                    # the device parameters keep their old values
+
+
+def test_offload_rejects(abi):
+    g, p, m, v = _inputs(100, "bf16", 2)
+    with pytest.raises(ValueError):               # the binding refuses a staging tensor below the minimum
+        _offload(abi, g, p, m, v, "bf16", "bf16", 1, 1.0, 0, 512)
+    with pytest.raises(abi.ZeroError) as e:       # and so does the library, for a declared size below it
+        _offload(abi, g, p, m, v, "bf16", "bf16", 1, 1.0, 0, 576, declared=512)
+    assert e.value.code == abi.ZERO_EINVAL
+    with pytest.raises(abi.ZeroError) as e:       # a clip multiplier of zero on the device
+        _offload(abi, g, p, m, v, "bf16", "bf16", 1, 0.0, 0, 576)
+    assert e.value.code == abi.ZERO_EINVAL and "clip multiplier" in str(e.value)
+    got = _offload(abi, g, p, m, v, "bf16", "bf16", 1, 1.0, 0, 576)     # and the next call works
+    assert not np.array_equal(got[0], p)

@@ -34,7 +34,7 @@ def _note(msg):
 
 
 def _np32(t):
-    return t.detach().cpu().numpy()
+    return t.detach().cpu().numpy().copy()      # a copy: host-resident state is updated in place
 
 
 def _hp(w):
@@ -101,6 +101,7 @@ SHRUNK = {
     # layouts, fewer elements; max_norm lowered so clipping stays active at
     # the smaller norms (about 0.016, 0.15, 0.078 and 0.10).
     "llama3_8b_nd8_z2": dict(psi=8 * 200_001 + 5, units=(8 * 200_001 + 5,), max_norm=0.01),
+    "llama3_8b_nd8_z2_offload": dict(psi=8 * 200_001 + 5, units=(8 * 200_001 + 5,), max_norm=0.01),
     "paper_7p5b_nd64_z3": dict(psi=6 * 156_250, units=(156_250,) * 6, max_norm=0.1),
     "paper_7p5b_nd64_z3_qwz8": dict(psi=6 * 156_250, units=(156_250,) * 6, max_norm=0.1),
     "paper_7p5b_nd64_z3_qwz4": dict(psi=6 * 156_250, units=(156_250,) * 6, max_norm=0.1),

@@ -128,7 +128,7 @@ def _period_sumsq(reduced_period, tail_len, n, dtype, inv_s):
     return (n // len(reduced_period)) * whole + tail
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_nd8_z2", "gpt2_1p5b_nd16_z1", "paper_7p5b_nd64_z3",
+@pytest.mark.parametrize("name", ["llama3_8b_nd8_z2", "llama3_8b_nd8_z2_offload", "gpt2_1p5b_nd16_z1", "paper_7p5b_nd64_z3",
                                   "paper_7p5b_nd64_z3_qwz8", "paper_7p5b_nd64_z3_qwz4", "gpt3_175b_nd16_z1"])
 def test_full_size_step(runner, name):
     w = workloads.get(name)
@@ -152,7 +152,7 @@ def test_full_size_step(runner, name):
     chunks = {}
     for o in offs:
         contribs, grad = grads_at(o, o + CHUNK)
-        state = tuple(t[0, o:o + CHUNK].cpu().numpy() for t in (run.master, run.m, run.v))
+        state = tuple(t[0, o:o + CHUNK].cpu().numpy().copy() for t in (run.master, run.m, run.v))
         chunks[o] = (contribs, grad, state)
     others = None
     if run.shards is not None:

@@ -36,9 +36,13 @@ EXPORTED = (
     "zero_workspace_bytes", "zero_reduce_shard", "zero_grad_norm", "zero_adam_step",
     "zero_gather_params", "zero_last_error", "zero_version",
     "zero_quant_code_bytes", "zero_quant_scale_count", "zero_quantize_blocks", "zero_dequantize_blocks",
-    "zero_gather_dequant",
+    "zero_gather_dequant", "zero_cpu_adam_step", "zero_offload_adam_step", "zero_cpu_isa", "zero_cpu_set_isa",
 )
 ZERO_QBLOCK = 256
+ZERO_CPU_SCALAR = 0
+ZERO_CPU_AVX2 = 1
+ZERO_CPU_AVX512 = 2
+ZERO_OFFLOAD_MIN_STAGING = 576
 
 
 class ZeroError(RuntimeError):
@@ -92,6 +96,12 @@ _sig = {
     "zero_quantize_blocks": (_I, [_P, _I, _I64, _I, _P, _P, _P]),
     "zero_dequantize_blocks": (_I, [_P, _P, _I64, _I, _P, _I, _P]),
     "zero_gather_dequant": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _I, _I, _I, _P, _P, _I64, _P]),
+    "zero_cpu_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), ctypes.c_float, _I,
+                                _P, _I, _I]),
+    "zero_offload_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
+                                    _P, _I64, _I, _P]),
+    "zero_cpu_isa": (_I, []),
+    "zero_cpu_set_isa": (_I, [_I]),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_version": (_I, []),
 }
@@ -128,6 +138,19 @@ def _need(x, nbytes, what):
         return
     if not x.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes, needs {nbytes}")
+
+
+def _need_host(x, nbytes, what):
+    """A tensor argument must be a contiguous host tensor holding nbytes."""
+    if x is None or isinstance(x, int) or nbytes <= 0:
+        return
+    if x.is_cuda:
+        raise ValueError(f"{what} must be a host tensor")
     if not x.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     have = x.numel() * x.element_size()
@@ -399,3 +422,39 @@ def zero_gather_dequant(plan, code_shards, scale_shards, unit_begin, unit_end, b
     sp = _table(scale_shards, scale_bytes, "scale shard")
     _check(lib.zero_gather_dequant(handle, cp, sp, int(unit_begin), int(unit_end), int(bits), _dtype(dtype),
                                    _ptr(full), _ptr(workspace), wb, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# CPU-offloaded optimizer (ZeRO-Offload)
+# ---------------------------------------------------------------------------
+
+def zero_cpu_isa():
+    return lib.zero_cpu_isa()
+
+
+def zero_cpu_set_isa(isa):
+    _check(lib.zero_cpu_set_isa(int(isa)))
+
+
+def zero_cpu_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, skip, param_out, param_dtype, n_threads):
+    for t, b, what in ((master, 4 * n, "master"), (m, 4 * n, "m"), (v, 4 * n, "v"), (grad, 2 * n, "grad"),
+                       (param_out, 2 * n, "param_out")):
+        _need_host(t, b, what)
+    _check(lib.zero_cpu_adam_step(_ptr(master), _ptr(m), _ptr(v), _ptr(grad), _dtype(grad_dtype), int(n),
+                                  ctypes.byref(hp), float(coef), int(bool(skip)), _ptr(param_out),
+                                  _dtype(param_dtype), int(n_threads)))
+
+
+def zero_offload_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, flag, param_out, param_dtype, staging,
+                           n_threads, stream=None, staging_bytes=None):
+    for t, b, what in ((master, 4 * n, "master"), (m, 4 * n, "m"), (v, 4 * n, "v")):
+        _need_host(t, b, what)
+    _need_host(staging, ZERO_OFFLOAD_MIN_STAGING, "staging")
+    for t, b, what in ((grad, 2 * n, "grad"), (param_out, 2 * n, "param_out"), (coef, 4, "coef"),
+                       (flag, 4, "flag")):
+        _need(t, b, what)
+    sb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(lib.zero_offload_adam_step(_ptr(master), _ptr(m), _ptr(v), _ptr(grad), _dtype(grad_dtype), int(n),
+                                      ctypes.byref(hp), _ptr(coef), _ptr(flag), _ptr(param_out),
+                                      _dtype(param_dtype), _ptr(staging), int(sb), int(n_threads),
+                                      _stream(stream)))

@@ -15,6 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libzero_flat.so")
 ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 def _hipcc():
@@ -22,6 +23,13 @@ def _hipcc():
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found")
+
+
+def _cxx():
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
 
 
 def _run(cmd):
@@ -38,6 +46,12 @@ def build(verbose=True):
     plan_o = os.path.join(objdir, "plan.o")
     _run([hipcc, *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
     objs = [plan_o]
+    # Host AdamW (host code only, built by the host compiler): IEEE fp32 with no
+    # contraction, so every instruction set gives the same bits.
+    offload_o = os.path.join(objdir, "offload.o")
+    _run([_cxx(), *common, "-ffp-contract=off", f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__",
+          "-c", os.path.join(CSRC, "offload.cpp"), "-o", offload_o])
+    objs.append(offload_o)
     for src in ("kernels.hip", "quant.hip"):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         _run([hipcc, *common, "-x", "hip", f"--offload-arch={ARCH}",

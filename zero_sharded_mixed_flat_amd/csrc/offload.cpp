@@ -1,0 +1,445 @@
+// CPU-offloaded optimizer (ZeRO-Offload): AdamW on host-resident fp32 state,
+// and the step that streams the reduced gradient from HBM to the host, runs
+// the host AdamW chunk by chunk and streams the 16-bit parameters back.
+//
+// ZeRO-Offload keeps only the 16-bit parameters and gradients on the GPU and
+// moves the fp32 master, m and v (12 bytes per parameter) to host memory,
+// where a multi-threaded, vectorised Adam updates them; each step sends the
+// gradient to the host and the 16-bit parameters back (L18 notes §4.4).
+//
+// Arithmetic: the same fp32 operation sequence as the GPU kernel, in IEEE
+// single precision with no fused multiply-add, so the AVX-512, AVX2 and scalar
+// paths give identical bits on every x86-64 host.  fp16 conversions use the
+// F16C instructions on the vector paths (round to nearest even) and an exact
+// software conversion on the scalar path; bf16 uses integer rounding.
+
+#include <hip/hip_runtime_api.h>
+#include <immintrin.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+namespace zf {
+namespace {
+
+struct HostAdam {
+    float lr, b1, b2, omb1, omb2, eps, wd, gs, inv_bc1, inv_bc2;
+};
+
+// ---------------------------------------------------------------------------
+// scalar 16-bit <-> fp32, exact, from the IEEE 754 encodings
+// ---------------------------------------------------------------------------
+
+inline float bits_to_float(uint32_t u) {
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+inline uint32_t float_to_bits(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return u;
+}
+
+inline float widen_scalar(uint16_t b, int dt) {
+    if (dt == ZERO_BF16) return bits_to_float(uint32_t(b) << 16);
+    const uint32_t sign = uint32_t(b & 0x8000u) << 16;
+    const uint32_t e = (b >> 10) & 0x1fu, mant = b & 0x3ffu;
+    if (e == 0x1f) return bits_to_float(sign | 0x7f800000u | (mant << 13));
+    if (e == 0) {
+        const float mag = float(mant) * 0x1p-24f;  // subnormal: mant units of 2^-24, exact
+        return sign ? -mag : mag;
+    }
+    return bits_to_float(sign | ((e + 112u) << 23) | (mant << 13));
+}
+
+inline uint16_t narrow_scalar(float x, int dt) {
+    uint32_t u = float_to_bits(x);
+    if (dt == ZERO_BF16) {
+        if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+        return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    const uint16_t sign = uint16_t((u >> 16) & 0x8000u);
+    u &= 0x7fffffffu;
+    if (u > 0x7f800000u) return sign | 0x7e00u;        // NaN
+    if (u >= 0x477ff000u) return sign | 0x7c00u;       // at least 65520: rounds to infinity
+    if (u >= 0x38800000u) {                            // normal fp16 range (>= 2^-14)
+        uint32_t r = u - 0x38000000u;                  // rebias the exponent by 127 - 15
+        r += 0x0fffu + ((r >> 13) & 1u);               // round to nearest even on 13 dropped bits
+        return uint16_t(sign | (r >> 13));
+    }
+    if (u <= 0x33000000u) return sign;                 // at most 2^-25: rounds to zero
+    const uint32_t e = u >> 23, m = (u & 0x7fffffu) | 0x800000u;
+    const uint32_t shift = 126u - e;                   // value = m * 2^(e - 150) = (m >> shift) units of 2^-24
+    uint32_t q = m >> shift;
+    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1u);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    return uint16_t(sign | q);
+}
+
+inline void adam_scalar(const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt,
+                        uint16_t* out, int pdt, int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+        const float g = widen_scalar(g16[i], gdt) * c.gs;
+        const float mm = c.b1 * m[i] + c.omb1 * g;
+        const float vv = c.b2 * v[i] + c.omb2 * (g * g);
+        const float denom = std::sqrt(vv * c.inv_bc2) + c.eps;
+        const float pp = p[i] - c.lr * ((mm * c.inv_bc1) / denom + c.wd * p[i]);
+        m[i] = mm;
+        v[i] = vv;
+        p[i] = pp;
+        out[i] = narrow_scalar(pp, pdt);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// AVX-512: 16 elements per iteration
+// ---------------------------------------------------------------------------
+
+__attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) void adam_avx512(
+    const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt, uint16_t* out, int pdt,
+    int64_t lo, int64_t hi) {
+    const __m512 b1 = _mm512_set1_ps(c.b1), b2 = _mm512_set1_ps(c.b2), omb1 = _mm512_set1_ps(c.omb1),
+                 omb2 = _mm512_set1_ps(c.omb2), eps = _mm512_set1_ps(c.eps), lr = _mm512_set1_ps(c.lr),
+                 wd = _mm512_set1_ps(c.wd), gs = _mm512_set1_ps(c.gs), ibc1 = _mm512_set1_ps(c.inv_bc1),
+                 ibc2 = _mm512_set1_ps(c.inv_bc2);
+    const __m512i abs_mask = _mm512_set1_epi32(0x7fffffff), inf = _mm512_set1_epi32(0x7f800000),
+                  round = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1),
+                  qnan = _mm512_set1_epi32(0x7fc0);
+    int64_t i = lo;
+    for (; i + 16 <= hi; i += 16) {
+        const __m256i graw = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(g16 + i));
+        __m512 g = gdt == ZERO_BF16 ? _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(graw), 16))
+                                    : _mm512_cvtph_ps(graw);
+        g = _mm512_mul_ps(g, gs);
+        const __m512 pv = _mm512_loadu_ps(p + i);
+        const __m512 mm = _mm512_add_ps(_mm512_mul_ps(b1, _mm512_loadu_ps(m + i)), _mm512_mul_ps(omb1, g));
+        const __m512 vv =
+            _mm512_add_ps(_mm512_mul_ps(b2, _mm512_loadu_ps(v + i)), _mm512_mul_ps(omb2, _mm512_mul_ps(g, g)));
+        const __m512 denom = _mm512_add_ps(_mm512_sqrt_ps(_mm512_mul_ps(vv, ibc2)), eps);
+        const __m512 upd = _mm512_add_ps(_mm512_div_ps(_mm512_mul_ps(mm, ibc1), denom), _mm512_mul_ps(wd, pv));
+        const __m512 pp = _mm512_sub_ps(pv, _mm512_mul_ps(lr, upd));
+        _mm512_storeu_ps(m + i, mm);
+        _mm512_storeu_ps(v + i, vv);
+        _mm512_storeu_ps(p + i, pp);
+        __m256i o;
+        if (pdt == ZERO_BF16) {
+            const __m512i u = _mm512_castps_si512(pp);
+            const __mmask16 nan = _mm512_cmpgt_epi32_mask(_mm512_and_si512(u, abs_mask), inf);
+            const __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u, 16), one);
+            __m512i r = _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(u, round), lsb), 16);
+            r = _mm512_mask_mov_epi32(r, nan, qnan);
+            o = _mm512_cvtepi32_epi16(r);
+        } else {
+            o = _mm512_cvtps_ph(pp, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+        }
+        _mm256_storeu_si256(reinterpret_cast<__m256i*>(out + i), o);
+    }
+    adam_scalar(c, p, m, v, g16, gdt, out, pdt, i, hi);
+}
+
+// ---------------------------------------------------------------------------
+// AVX2: 8 elements per iteration
+// ---------------------------------------------------------------------------
+
+__attribute__((target("avx2,f16c"))) void adam_avx2(const HostAdam& c, float* p, float* m, float* v,
+                                                     const uint16_t* g16, int gdt, uint16_t* out, int pdt,
+                                                     int64_t lo, int64_t hi) {
+    const __m256 b1 = _mm256_set1_ps(c.b1), b2 = _mm256_set1_ps(c.b2), omb1 = _mm256_set1_ps(c.omb1),
+                 omb2 = _mm256_set1_ps(c.omb2), eps = _mm256_set1_ps(c.eps), lr = _mm256_set1_ps(c.lr),
+                 wd = _mm256_set1_ps(c.wd), gs = _mm256_set1_ps(c.gs), ibc1 = _mm256_set1_ps(c.inv_bc1),
+                 ibc2 = _mm256_set1_ps(c.inv_bc2);
+    const __m256i abs_mask = _mm256_set1_epi32(0x7fffffff), inf = _mm256_set1_epi32(0x7f800000),
+                  round = _mm256_set1_epi32(0x7fff), one = _mm256_set1_epi32(1),
+                  qnan = _mm256_set1_epi32(0x7fc0);
+    int64_t i = lo;
+    for (; i + 8 <= hi; i += 8) {
+        const __m128i graw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(g16 + i));
+        __m256 g = gdt == ZERO_BF16 ? _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(graw), 16))
+                                    : _mm256_cvtph_ps(graw);
+        g = _mm256_mul_ps(g, gs);
+        const __m256 pv = _mm256_loadu_ps(p + i);
+        const __m256 mm = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(m + i)), _mm256_mul_ps(omb1, g));
+        const __m256 vv =
+            _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(v + i)), _mm256_mul_ps(omb2, _mm256_mul_ps(g, g)));
+        const __m256 denom = _mm256_add_ps(_mm256_sqrt_ps(_mm256_mul_ps(vv, ibc2)), eps);
+        const __m256 upd = _mm256_add_ps(_mm256_div_ps(_mm256_mul_ps(mm, ibc1), denom), _mm256_mul_ps(wd, pv));
+        const __m256 pp = _mm256_sub_ps(pv, _mm256_mul_ps(lr, upd));
+        _mm256_storeu_ps(m + i, mm);
+        _mm256_storeu_ps(v + i, vv);
+        _mm256_storeu_ps(p + i, pp);
+        __m128i o;
+        if (pdt == ZERO_BF16) {
+            const __m256i u = _mm256_castps_si256(pp);
+            const __m256i nan = _mm256_cmpgt_epi32(_mm256_and_si256(u, abs_mask), inf);
+            const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), one);
+            __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, round), lsb), 16);
+            r = _mm256_blendv_epi8(r, qnan, nan);
+            o = _mm_packus_epi32(_mm256_castsi256_si128(r), _mm256_extracti128_si256(r, 1));
+        } else {
+            o = _mm256_cvtps_ph(pp, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+        }
+        _mm_storeu_si128(reinterpret_cast<__m128i*>(out + i), o);
+    }
+    adam_scalar(c, p, m, v, g16, gdt, out, pdt, i, hi);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch and threads
+// ---------------------------------------------------------------------------
+
+int detect_isa() {
+    __builtin_cpu_init();
+    if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+        __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("f16c"))
+        return ZERO_CPU_AVX512;
+    if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("f16c")) return ZERO_CPU_AVX2;
+    return ZERO_CPU_SCALAR;
+}
+
+const int g_detected_isa = detect_isa();
+std::atomic<int> g_isa{g_detected_isa};
+
+void adam_range(int isa, const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt,
+                uint16_t* out, int pdt, int64_t lo, int64_t hi) {
+    if (isa == ZERO_CPU_AVX512)
+        adam_avx512(c, p, m, v, g16, gdt, out, pdt, lo, hi);
+    else if (isa == ZERO_CPU_AVX2)
+        adam_avx2(c, p, m, v, g16, gdt, out, pdt, lo, hi);
+    else
+        adam_scalar(c, p, m, v, g16, gdt, out, pdt, lo, hi);
+}
+
+constexpr int kMaxThreads = 256;
+constexpr int64_t kMinPerThread = 1 << 15;  // smaller ranges are not worth a thread
+
+// Split [0, n) into contiguous, 64-element-aligned ranges, one per thread; the
+// calling thread takes the first.
+void adam_threads(const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt, uint16_t* out,
+                  int pdt, int64_t n, int n_threads) {
+    const int isa = g_isa.load();
+    const int64_t by_size = std::max<int64_t>(1, n / kMinPerThread);
+    const int t = int(std::min<int64_t>(n_threads, by_size));
+    if (t <= 1) {
+        adam_range(isa, c, p, m, v, g16, gdt, out, pdt, 0, n);
+        return;
+    }
+    const int64_t per = ((n + t - 1) / t + 63) / 64 * 64;
+    std::vector<std::thread> pool;
+    pool.reserve(t - 1);
+    for (int k = 1; k < t; ++k) {
+        const int64_t lo = std::min<int64_t>(n, k * per), hi = std::min<int64_t>(n, lo + per);
+        if (lo >= hi) break;
+        pool.emplace_back(adam_range, isa, std::cref(c), p, m, v, g16, gdt, out, pdt, lo, hi);
+    }
+    adam_range(isa, c, p, m, v, g16, gdt, out, pdt, 0, std::min<int64_t>(n, per));
+    for (auto& th : pool) th.join();
+}
+
+constexpr int64_t kOffloadMinStaging = ZERO_OFFLOAD_MIN_STAGING;  // head room + four slots of 64 values
+static_assert(ZERO_OFFLOAD_MIN_STAGING == 64 + 8 * 64, "staging layout");
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(ZERO_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool valid_dtype_h(int dt) { return dt == ZERO_F16 || dt == ZERO_BF16; }
+
+uintptr_t addr_h(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+
+bool overlaps_h(const void* a, int64_t ab, const void* b, int64_t bb) {
+    if (ab <= 0 || bb <= 0) return false;
+    return addr_h(a) < addr_h(b) + uintptr_t(bb) && addr_h(b) < addr_h(a) + uintptr_t(ab);
+}
+
+bool pow2_positive_h(float x) {
+    if (!(x > 0.0f) || !std::isfinite(x)) return false;
+    int e;
+    return std::frexp(x, &e) == 0.5f;
+}
+
+// Shared validation of the hyperparameters; fills the fp32 constants.
+int make_consts(const char* fn, const zero_adam_hparams* hp, float coef, HostAdam* c) {
+    if (hp == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": hp is NULL");
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
+        !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(ZERO_EINVAL, std::string(fn) + ": hyperparameters must be finite, betas in [0, 1)");
+    if (hp->step < 1) return fail(ZERO_EINVAL, std::string(fn) + ": step must be >= 1");
+    if (!pow2_positive_h(hp->inv_loss_scale))
+        return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
+    if (!std::isfinite(coef) || !(coef > 0.0f))
+        return fail(ZERO_EINVAL, std::string(fn) + ": coef must be finite and positive");
+    const float bc1 = float(1.0 - std::pow(double(hp->beta1), double(hp->step)));
+    const float bc2 = float(1.0 - std::pow(double(hp->beta2), double(hp->step)));
+    if (!(bc1 > 0.0f) || !(bc2 > 0.0f)) return fail(ZERO_EINVAL, std::string(fn) + ": bias correction is zero");
+    c->lr = hp->lr;
+    c->b1 = hp->beta1;
+    c->b2 = hp->beta2;
+    c->omb1 = float(1.0 - double(hp->beta1));
+    c->omb2 = float(1.0 - double(hp->beta2));
+    c->eps = hp->eps;
+    c->wd = hp->weight_decay;
+    c->gs = hp->inv_loss_scale * coef;
+    c->inv_bc1 = float(1.0 / double(bc1));
+    c->inv_bc2 = float(1.0 / double(bc2));
+    return ZERO_OK;
+}
+
+int check_host_buffers(const char* fn, float* master, float* m, float* v, const void* grad, const void* param,
+                       int64_t n) {
+    if (!master || !m || !v || !grad || !param) return fail(ZERO_EINVAL, std::string(fn) + ": NULL buffer");
+    if ((addr_h(master) | addr_h(m) | addr_h(v)) & 3)
+        return fail(ZERO_EINVAL, std::string(fn) + ": fp32 buffers must be 4-byte aligned");
+    if ((addr_h(grad) | addr_h(param)) & 1)
+        return fail(ZERO_EINVAL, std::string(fn) + ": 16-bit buffers must be 2-byte aligned");
+    const void* outs[4] = {master, m, v, param};
+    const int64_t ob[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps_h(outs[i], ob[i], outs[j], ob[j]))
+                return fail(ZERO_EALIAS, std::string(fn) + ": master, m, v and the parameters must not overlap");
+        if (overlaps_h(outs[i], ob[i], grad, 2 * n))
+            return fail(ZERO_EALIAS, std::string(fn) + ": an output overlaps the gradient");
+    }
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zf
+
+using namespace zf;
+
+extern "C" {
+
+int zero_cpu_isa(void) { return g_isa.load(); }
+
+int zero_cpu_set_isa(int isa) {
+    if (isa < ZERO_CPU_SCALAR || isa > g_detected_isa)
+        return fail(ZERO_EINVAL, "zero_cpu_set_isa: not supported by this CPU");
+    g_isa.store(isa);
+    return ok();
+}
+
+int zero_cpu_adam_step(float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
+                       const zero_adam_hparams* hp, float coef, int skip, void* param_out, int param_dtype,
+                       int n_threads) {
+    const char* fn = "zero_cpu_adam_step";
+    if (n < 0) return fail(ZERO_EINVAL, std::string(fn) + ": n < 0");
+    if (!valid_dtype_h(grad_dtype) || !valid_dtype_h(param_dtype))
+        return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
+    if (n_threads < 1 || n_threads > kMaxThreads)
+        return fail(ZERO_EINVAL, std::string(fn) + ": n_threads must be in [1, 256]");
+    HostAdam c;
+    if (int rc = make_consts(fn, hp, coef, &c)) return rc;
+    if (n == 0 || skip) return ok();
+    if (int rc = check_host_buffers(fn, master, m, v, grad, param_out, n)) return rc;
+    adam_threads(c, master, m, v, static_cast<const uint16_t*>(grad), grad_dtype, static_cast<uint16_t*>(param_out),
+                 param_dtype, n, n_threads);
+    return ok();
+}
+
+int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_dev, int grad_dtype, int64_t n,
+                           const zero_adam_hparams* hp, const float* coef_dev, const int32_t* flag_dev,
+                           void* param_dev, int param_dtype, void* staging, int64_t staging_bytes, int n_threads,
+                           void* stream) {
+    const char* fn = "zero_offload_adam_step";
+    if (n < 0) return fail(ZERO_EINVAL, std::string(fn) + ": n < 0");
+    if (!valid_dtype_h(grad_dtype) || !valid_dtype_h(param_dtype))
+        return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
+    if (n_threads < 1 || n_threads > kMaxThreads)
+        return fail(ZERO_EINVAL, std::string(fn) + ": n_threads must be in [1, 256]");
+    HostAdam c;
+    if (int rc = make_consts(fn, hp, 1.0f, &c)) return rc;
+    if (coef_dev == nullptr || (addr_h(coef_dev) & 3) || flag_dev == nullptr || (addr_h(flag_dev) & 3))
+        return fail(ZERO_EINVAL, std::string(fn) + ": coef_dev or flag NULL or misaligned");
+    if (n == 0) return ok();
+    if (int rc = check_host_buffers(fn, master, m, v, grad_dev, param_dev, n)) return rc;
+    if (staging == nullptr || (addr_h(staging) & 63) || staging_bytes < kOffloadMinStaging)
+        return fail(ZERO_EINVAL, std::string(fn) + ": staging must be 64-byte aligned and at least " +
+                                     std::to_string(kOffloadMinStaging) + " bytes");
+    if (overlaps_h(staging, staging_bytes, master, 4 * n) || overlaps_h(staging, staging_bytes, m, 4 * n) ||
+        overlaps_h(staging, staging_bytes, v, 4 * n))
+        return fail(ZERO_EALIAS, std::string(fn) + ": staging overlaps the host state");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Staging: 8 bytes of head room for the clip multiplier and the flag, then
+    // two gradient slots and two parameter slots of `chunk` 16-bit values.
+    char* st = static_cast<char*>(staging);
+    float* coef_h = reinterpret_cast<float*>(st);
+    int32_t* flag_h = reinterpret_cast<int32_t*>(st + 4);
+    const int64_t chunk = std::min<int64_t>(n, (staging_bytes - 64) / 8 / 64 * 64);
+    uint16_t* gslot[2] = {reinterpret_cast<uint16_t*>(st + 64), reinterpret_cast<uint16_t*>(st + 64) + chunk};
+    uint16_t* pslot[2] = {gslot[1] + chunk, gslot[1] + 2 * chunk};
+    const uint16_t* g_dev = static_cast<const uint16_t*>(grad_dev);
+    uint16_t* p_dev = static_cast<uint16_t*>(param_dev);
+
+    auto status = [&](hipError_t e) { return e == hipSuccess ? ZERO_OK : hip_fail(e, fn); };
+    hipEvent_t got[2] = {nullptr, nullptr}, sent[2] = {nullptr, nullptr};
+    int rc = ZERO_OK;
+    for (int k = 0; k < 2 && rc == ZERO_OK; ++k) {
+        rc = status(hipEventCreateWithFlags(&got[k], hipEventDisableTiming));
+        if (rc == ZERO_OK) rc = status(hipEventCreateWithFlags(&sent[k], hipEventDisableTiming));
+    }
+    auto cleanup = [&]() {
+        for (int k = 0; k < 2; ++k) {
+            if (got[k]) (void)hipEventDestroy(got[k]);
+            if (sent[k]) (void)hipEventDestroy(sent[k]);
+        }
+    };
+    if (rc != ZERO_OK) {
+        cleanup();
+        return rc;
+    }
+    // The clip multiplier and the skip flag come first: the update needs both.
+    rc = status(hipMemcpyAsync(coef_h, coef_dev, 4, hipMemcpyDeviceToHost, s));
+    if (rc == ZERO_OK) rc = status(hipMemcpyAsync(flag_h, flag_dev, 4, hipMemcpyDeviceToHost, s));
+    if (rc == ZERO_OK) rc = status(hipStreamSynchronize(s));
+    if (rc == ZERO_OK && *flag_h != 0) {  // skipped step: nothing moves
+        cleanup();
+        return ok();
+    }
+    if (rc == ZERO_OK && !(std::isfinite(*coef_h) && *coef_h > 0.0f))
+        rc = fail(ZERO_EINVAL, std::string(fn) + ": the clip multiplier on the device is not finite and positive");
+    if (rc == ZERO_OK) c.gs = hp->inv_loss_scale * *coef_h;
+
+    // Chunk k: gradient in (slot k%2) -> host AdamW -> parameters out (slot k%2).
+    // The copy of chunk k+1 is queued before chunk k is updated, and a slot's
+    // parameters are rewritten only after their copy to the device is done.
+    const int64_t n_chunks = (n + chunk - 1) / chunk;
+    auto enqueue_in = [&](int64_t k) {
+        const int64_t lo = k * chunk, len = std::min(chunk, n - lo);
+        hipError_t e = hipMemcpyAsync(gslot[k & 1], g_dev + lo, 2 * len, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipEventRecord(got[k & 1], s);
+        return status(e);
+    };
+    if (rc == ZERO_OK) rc = enqueue_in(0);
+    bool sent_pending[2] = {false, false};
+    for (int64_t k = 0; k < n_chunks && rc == ZERO_OK; ++k) {
+        const int64_t lo = k * chunk, len = std::min(chunk, n - lo);
+        if (k + 1 < n_chunks) rc = enqueue_in(k + 1);
+        if (rc == ZERO_OK) rc = status(hipEventSynchronize(got[k & 1]));
+        if (rc == ZERO_OK && sent_pending[k & 1]) rc = status(hipEventSynchronize(sent[k & 1]));
+        if (rc != ZERO_OK) break;
+        adam_threads(c, master + lo, m + lo, v + lo, gslot[k & 1], grad_dtype, pslot[k & 1], param_dtype, len,
+                     n_threads);
+        rc = status(hipMemcpyAsync(p_dev + lo, pslot[k & 1], 2 * len, hipMemcpyHostToDevice, s));
+        if (rc == ZERO_OK) rc = status(hipEventRecord(sent[k & 1], s));
+        sent_pending[k & 1] = true;
+    }
+    // The staging buffer is the caller's again only once every copy has ended.
+    const hipError_t e = hipStreamSynchronize(s);
+    if (rc == ZERO_OK) rc = status(e);
+    cleanup();
+    return rc == ZERO_OK ? ok() : rc;
+}
+
+}  // extern "C"

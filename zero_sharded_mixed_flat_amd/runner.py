@@ -15,14 +15,25 @@ With a block-quantised gather (ZeRO++ quantised weights) the last step is
     per-unit gather of every rank's codes,
     dequantised into the 16-bit full buffer       zero_gather_dequant
 
-All calls go to one stream with no host synchronisation inside a step: the
-clip multiplier and the skip flag stay in device memory.  Contributions of the
+With ZeRO-Offload the fp32 state is in host memory and the AdamW step is
+
+    gradient to the host, host AdamW, 16-bit
+    parameters back, chunk by chunk               zero_offload_adam_step
+
+All calls go to one stream with no host synchronisation inside a step
+(except the offloaded update, which waits for its copies): the clip
+multiplier and the skip flag stay in device memory.  Contributions of the
 emulated ranks are buffers in this GPU's memory (one process, one GPU).
 """
+
+import os
 
 import torch
 
 from . import abi, synth
+
+OFFLOAD_CHUNK = 1 << 23          # values per staging slot of the offloaded update
+HOST_THREADS_MAX = 16
 
 TORCH16 = synth.TORCH_DTYPES
 
@@ -66,19 +77,21 @@ class RankStep:
         if not w.pre_reduced:
             self.reduced = torch.empty((len(self.owners), n), dtype=gdt, device=dev)
 
-        # fp32 optimizer state, one shard per emulated owner.
+        # fp32 optimizer state, one shard per emulated owner (in host memory,
+        # drawn on the GPU chunk by chunk, under ZeRO-Offload).
         k = len(self.owners)
-        self.master = torch.empty((k, n), dtype=torch.float32, device=dev)
-        self.m = torch.empty((k, n), dtype=torch.float32, device=dev)
-        self.v = torch.empty((k, n), dtype=torch.float32, device=dev)
+        state_dev = "cpu" if w.offload else dev
+        self.master = torch.empty((k, n), dtype=torch.float32, device=state_dev)
+        self.m = torch.empty((k, n), dtype=torch.float32, device=state_dev)
+        self.v = torch.empty((k, n), dtype=torch.float32, device=state_dev)
         for i, o in enumerate(self.owners):
-            synth.normal_(self.master[i], w.master_std, seed, 200 + o)
+            synth.normal_(self.master[i], w.master_std, seed, 200 + o, via=dev)
             if w.m_std:
-                synth.normal_(self.m[i], w.m_std, seed, 300 + o)
+                synth.normal_(self.m[i], w.m_std, seed, 300 + o, via=dev)
             else:
                 self.m[i].zero_()
             if w.v_std:
-                synth.abs_normal_(self.v[i], w.v_std, seed, 400 + o)
+                synth.abs_normal_(self.v[i], w.v_std, seed, 400 + o, via=dev)
             else:
                 self.v[i].zero_()
             if w.all_ranks:
@@ -120,6 +133,13 @@ class RankStep:
         if self.codes is not None:
             self.code_table = abi.PointerTable(list(self.codes), self.codes.shape[1], "code shard")
             self.scale_table = abi.PointerTable(list(self.scales), 4 * self.scales.shape[1], "scale shard")
+
+        # ZeRO-Offload: pinned staging for the chunked copies, host threads.
+        self.staging = None
+        self.host_threads = min(HOST_THREADS_MAX, len(os.sched_getaffinity(0)))
+        if w.offload:
+            chunk = min(OFFLOAD_CHUNK, max(64, n))
+            self.staging = torch.empty(64 + 8 * chunk, dtype=torch.uint8, pin_memory=True)
 
         n_sets = 1 if w.pre_reduced else len(self.owners)
         self.ws = torch.empty(abi.zero_workspace_bytes(n, n_sets), dtype=torch.uint8, device=dev)
@@ -189,8 +209,13 @@ class RankStep:
         w = self.w
         hp = self.hparams()
         for i in range(len(self.owners)):
-            abi.zero_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype, self.n,
-                               hp, self.coef, self.flag, self.param_out(i), w.param_dtype, stream)
+            if w.offload:
+                abi.zero_offload_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype,
+                                           self.n, hp, self.coef, self.flag, self.param_out(i), w.param_dtype,
+                                           self.staging, self.host_threads, stream)
+            else:
+                abi.zero_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype, self.n,
+                                   hp, self.coef, self.flag, self.param_out(i), w.param_dtype, stream)
 
     def quantize_shard(self, r, stream=None):
         abi.zero_quantize_blocks(self.shards[r], self.w.param_dtype, self.n, self.w.gather_bits, self.codes[r],
@@ -255,7 +280,12 @@ def phase_model(w, plan):
         out["reduce"] = {"kernel": "reduce_kernel", "launches": owners, "bytes_per_launch": (2 * w.nd + 2) * n}
     out["norm"] = {"kernel": "sumsq_kernel" if w.pre_reduced else "finalize_kernel", "launches": 1,
                    "bytes_per_launch": 2 * n if w.pre_reduced else 0}
-    out["adam"] = {"kernel": "adam_kernel", "launches": owners, "bytes_per_launch": 28 * n}
+    if w.offload:
+        # host memory traffic of the host AdamW (the same 28 bytes per element);
+        # the 4 bytes per element over PCIe are reported separately
+        out["adam"] = {"kernel": "host_adam", "launches": owners, "bytes_per_launch": 28 * n}
+    else:
+        out["adam"] = {"kernel": "adam_kernel", "launches": owners, "bytes_per_launch": 28 * n}
     if w.gather_bits != 16:
         code = abi.zero_quant_code_bytes(n, w.gather_bits) + 4 * abi.zero_quant_scale_count(n)
         out["quantize"] = {"kernel": "quantize_kernel", "launches": owners, "bytes_per_launch": 2 * n + code}

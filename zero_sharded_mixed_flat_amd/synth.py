@@ -43,16 +43,26 @@ def _chunks(t):
         yield ci, flat[lo:lo + CHUNK]
 
 
-def normal_(t, std, seed, stream):
-    """Fill ``t`` with N(0, std) in its own dtype."""
+def normal_(t, std, seed, stream, via=None):
+    """Fill ``t`` with N(0, std) in its own dtype.
+
+    With ``via`` (a device), each chunk is drawn there and copied into ``t``:
+    a host tensor filled via the GPU holds the same values as a GPU tensor
+    filled directly.
+    """
     for ci, piece in _chunks(t):
-        piece.normal_(0.0, std, generator=_gen(t.device, stream_seed(seed, stream, ci)))
+        g = _gen(via if via is not None else t.device, stream_seed(seed, stream, ci))
+        if via is None or torch.device(via).type == piece.device.type:
+            piece.normal_(0.0, std, generator=g)
+        else:
+            tmp = torch.empty(piece.shape, dtype=piece.dtype, device=via)
+            piece.copy_(tmp.normal_(0.0, std, generator=g))
     return t
 
 
-def abs_normal_(t, std, seed, stream):
+def abs_normal_(t, std, seed, stream, via=None):
     """Fill ``t`` with |N(0, std)|."""
-    normal_(t, std, seed, stream)
+    normal_(t, std, seed, stream, via)
     return t.abs_()
 
 

@@ -16,6 +16,10 @@ Shapes follow the pages' examples:
   bucket on 16 ranks under ZeRO-1, fp16 with a loss scale of 65536.
 * ``gpt3_175b_nd16_z1``: a 175e9-parameter vector (GPT-3 175B sized, Lecture 18
   notes §1.2) on 16 ranks; the rank's owner update on a pre-reduced gradient.
+* ``llama3_8b_nd8_z2_offload``: the LLaMA-3-8B-sized ZeRO-2 share with
+  ZeRO-Offload (Lecture 18 notes §4.4): master, m and v live in host memory
+  and the host AdamW updates them; the reduced gradient goes to the host and
+  the 16-bit parameters come back.
 * ``paper_7p5b_nd64_z3_qwz8`` / ``_qwz4``: the ZeRO-3 workload with the
   ZeRO++ quantised-weight gather (Lecture 18 notes §4.5): the rank quantises
   its updated 16-bit shard to INT8 / INT4 codes with one scale per 256
@@ -55,6 +59,7 @@ class Workload:
     gather_per_unit: bool = False # the 16-bit shards of every rank are gathered unit by unit
     gather_shard_std: float = 0.0 # other ranks' 16-bit parameter shards ~ N(0, this)
     gather_bits: int = 16         # 16: plain gather; 8 or 4: block-quantised codes
+    offload: bool = False         # fp32 state in host memory, AdamW on the CPU (ZeRO-Offload)
     steps: int = 1
     align: int = 8
     tensors: tuple = field(default=None, repr=False)   # ragged tensor sizes, if any
@@ -94,6 +99,12 @@ WORKLOADS = {
             master_std=0.02, m_std=1e-5, v_std=1e-8,
             lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
             rank=7),
+        Workload(
+            name="llama3_8b_nd8_z2_offload", psi=8_030_000_000, nd=8, stage=2, units=(8_030_000_000,),
+            grad_dtype="bf16", param_dtype="bf16", grad_std=1e-4,
+            master_std=0.02, m_std=1e-5, v_std=1e-8,
+            lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+            rank=7, offload=True),
         Workload(
             name="paper_7p5b_nd64_z3", psi=7_500_000_000, nd=64, stage=3,
             units=(156_250_000,) * 48,
