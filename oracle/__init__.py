@@ -16,7 +16,9 @@ master/m/v update, cast to the 16-bit parameter -- restricted to one rank's
 owned slice of the flat parameter vector:
 
 * ``partition``  -- flat-bucket ownership (Lecture 18 notes §3.2 and
-  exercise 6; Illustrated distributed training (8) ZeRO §8.4).  Integers only.
+  exercise 6; Illustrated distributed training (8) ZeRO §8.4), and restoring
+  sharded state under another partition (ZeRO reading notes 026 §五).
+  Integers only.
 * ``accounting`` -- per-rank model-state bytes 16Ψ, 4Ψ+KΨ/Nd, 2Ψ+(2+K)Ψ/Nd,
   (4+K)Ψ/Nd and communication volume 2Ψ / 3Ψ × (Nd−1)/Nd (Lecture 18 notes
   §2.1, §3.1; L3.2 Memory optimisation and ZeRO §2.3).
@@ -48,7 +50,7 @@ published formulas they restate, through library routines
 
 from . import accounting, partition, quant, rounding, step  # noqa: F401
 from .accounting import comm_volume, max_params, model_state_bytes  # noqa: F401
-from .partition import Plan, make_plan, segments, shard_of  # noqa: F401
+from .partition import Plan, make_plan, merge, reshard, reshard_segments, segments, shard_of  # noqa: F401
 from .rounding import narrow, widen  # noqa: F401
 from .step import (  # noqa: F401
     AdamHparams,

@@ -157,3 +157,73 @@ def unpad(plan, padded_full):
         raise ValueError("padded_full must hold exactly full_numel elements")
     return np.concatenate([padded_full[u.full_base:u.full_base + u.numel] for u in plan.units]) \
         if plan.units else padded_full[:0]
+
+
+# ---------------------------------------------------------------------------
+# Resharding (restoring sharded state under a different partition)
+# ---------------------------------------------------------------------------
+#
+# Pages: a checkpoint of sharded training holds each process's local slice of
+# the weights and optimizer state; restoring under a different degree of
+# parallelism has to re-own the state while keeping the parameter order and
+# which moment belongs to which parameter (026 notes §五).  Reading taken:
+# the flat parameter order (units concatenated) is the identity of a
+# parameter, so a restore is "merge every old shard into the flat vector, then
+# cut the new rank's shard out of it"; padding positions are zero.
+
+def merge(plan, shards):
+    """The unpadded flat vector (length psi) held by a complete set of shards."""
+    if len(shards) != plan.owners:
+        raise ValueError(f"need {plan.owners} shards, got {len(shards)}")
+    out = np.zeros(plan.psi, dtype=np.asarray(shards[0]).dtype)
+    flat_base = 0
+    for i, u in enumerate(plan.units):
+        for r in range(plan.owners):
+            lo, hi = plan.owned(r, i)
+            src = u.shard_base + (lo - r * u.slice_numel)
+            out[flat_base + lo:flat_base + hi] = np.asarray(shards[r])[src:src + (hi - lo)]
+        flat_base += u.numel
+    return out
+
+
+def reshard(old_plan, old_shards, new_plan, rank):
+    """Rank's shard under ``new_plan`` of the state held by ``old_shards`` under ``old_plan``."""
+    if old_plan.psi != new_plan.psi:
+        raise ValueError("the plans partition different parameter counts")
+    return shard_of(new_plan, merge(old_plan, old_shards), rank)
+
+
+def reshard_segments(old_plan, new_plan, rank):
+    """Where each element of rank's new shard comes from, as maximal runs.
+
+    Element by element: position j of the new shard holds flat parameter g (or
+    is padding); g lives in old owner r at old shard offset k.  Consecutive j
+    with the same r and consecutive k form one run (old_rank, old_offset,
+    new_offset, length), in new-shard order.  Padding is in no run.
+    """
+    if old_plan.psi != new_plan.psi:
+        raise ValueError("the plans partition different parameter counts")
+    # flat index -> (old owner, old shard offset), one element at a time
+    src_rank = np.empty(old_plan.psi, np.int64)
+    src_off = np.empty(old_plan.psi, np.int64)
+    flat_base = 0
+    for i, u in enumerate(old_plan.units):
+        for g in range(u.numel):
+            r = 0 if old_plan.owners == 1 else g // u.slice_numel
+            src_rank[flat_base + g] = r
+            src_off[flat_base + g] = u.shard_base + g - r * u.slice_numel
+        flat_base += u.numel
+    runs = []
+    flat_base = 0
+    for i, u in enumerate(new_plan.units):
+        lo, hi = new_plan.owned(rank, i)
+        r_new = 0 if new_plan.owners == 1 else rank
+        for g in range(lo, hi):
+            j = u.shard_base + g - r_new * u.slice_numel
+            r, k = int(src_rank[flat_base + g]), int(src_off[flat_base + g])
+            if runs and runs[-1][0] == r and runs[-1][1] + runs[-1][3] == k and runs[-1][2] + runs[-1][3] == j:
+                runs[-1][3] += 1
+            else:
+                runs.append([r, k, j, 1])
+        flat_base += u.numel
+    return [tuple(x) for x in runs]
