@@ -46,6 +46,7 @@ extern "C" {
 #define ZERO_EALIAS (-2)  /* an output overlaps an input or another output */
 #define ZERO_EHIP (-3)    /* the HIP runtime refused a launch or copy */
 #define ZERO_ENOMEM (-4)  /* host allocation for a plan failed */
+#define ZERO_EIO (-5)     /* a checkpoint file is missing, short, corrupt or unwritable */
 
 #define ZERO_F16 1
 #define ZERO_BF16 2
@@ -70,6 +71,15 @@ typedef struct {
     int64_t shard_off;  /* where the piece starts in the rank's shard */
     int64_t len;        /* elements */
 } zero_segment;
+
+/* A run of a restored shard: `len` elements at `new_offset` of the new shard
+ * come from old owner `old_rank`'s shard at `old_offset`. */
+typedef struct {
+    int64_t old_rank;
+    int64_t old_offset;
+    int64_t new_offset;
+    int64_t len;
+} zero_reshard_segment;
 
 /*
  * zero_plan_create -- flat-bucket partition of `n_units` units over `nd` ranks.
@@ -324,6 +334,69 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards,
                         const float* const* scale_shards, int unit_begin, int unit_end, int bits,
                         int dtype, void* full, void* workspace, int64_t workspace_bytes,
                         void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Sharded checkpoints and restoring under another partition               */
+/* ---------------------------------------------------------------------- */
+
+/* Where the arrays of a checkpoint call live. */
+#define ZERO_LOC_DEVICE 0
+#define ZERO_LOC_HOST 1 /* e.g. ZeRO-Offload's host-resident state */
+
+/* Elements per checksummed block of a checkpoint array (1 MiB of fp32), and
+ * the smallest staging buffer the checkpoint calls accept (two blocks). */
+#define ZERO_CKPT_BLOCK 262144
+#define ZERO_CKPT_MIN_STAGING (2 * 4 * ZERO_CKPT_BLOCK)
+
+/*
+ * zero_plan_reshard -- restoring sharded state under another partition has to
+ * re-own it while keeping the parameter order and which moment belongs to
+ * which parameter (026 notes §五).  The flat parameter order (units
+ * concatenated) identifies a parameter, so rank `new_rank`'s shard under
+ * `new_plan` is filled by maximal runs copied from the shards of `old_plan`,
+ * in new-shard order; positions in no run are padding (zero).  The plans may
+ * differ in Nd, stage, units and align but must partition the same number of
+ * parameters.  Writes at most `cap` runs and the total to *count (cap = 0 to
+ * size the array).  Errors: ZERO_EINVAL (NULL, rank, parameter counts).
+ */
+int zero_plan_reshard(const zero_plan* old_plan, const zero_plan* new_plan, int new_rank,
+                      zero_reshard_segment* out, int cap, int* count);
+
+/*
+ * zero_ckpt_save -- writes rank `rank`'s optimizer state (master, m, v: fp32,
+ * the plan's shard_numel each, padding included) and the plan to one file per
+ * rank, so a restore can rebuild the old partition (026 notes §五; L3.2 §4.3:
+ * a resumable checkpoint holds the sharded optimizer state, not only the
+ * weights).  Layout: a 4 KiB-aligned header (magic, version, Nd, stage,
+ * align, rank, step, the unit sizes, one 64-bit checksum per 1 MiB block of
+ * each array), then the three arrays.  The file is written as `path`.tmp and
+ * renamed, so `path` never names a partial file.  `location`: ZERO_LOC_DEVICE
+ * (arrays in device memory, copied out through `staging` on `stream`) or
+ * ZERO_LOC_HOST.  staging: pinned host memory, >= ZERO_CKPT_MIN_STAGING
+ * bytes, 64-byte aligned.  Blocks until the file is complete.  Errors:
+ * ZERO_EINVAL, ZERO_EIO (with the path and the system's reason), ZERO_EHIP.
+ */
+int zero_ckpt_save(const char* path, const zero_plan* plan, int rank, int64_t step,
+                   const float* master, const float* m, const float* v, int location,
+                   void* staging, int64_t staging_bytes, void* stream);
+
+/*
+ * zero_ckpt_load -- restores rank `rank`'s shard under `plan` from the files
+ * of ALL ranks of a saved run (paths[i] is old rank i's file, n_paths the old
+ * owner count).  Every file must exist and agree (the same run, step, plan
+ * and parameter count as `plan`), whether or not this rank reads from it, so a
+ * missing or foreign file fails explicitly instead of yielding an incomplete
+ * model.  The runs of zero_plan_reshard are read block by block; every block
+ * read is checked against its stored checksum; positions in no run are set to
+ * zero.  master, m, v: the plan's shard_numel fp32 each, in `location`.
+ * *step_out: the saved step count.  staging as for zero_ckpt_save.  Blocks
+ * until the state is in place.  Errors: ZERO_EIO (missing, short or corrupt
+ * file, naming its rank and path), ZERO_EINVAL (mismatched files or plans,
+ * arguments), ZERO_EHIP.
+ */
+int zero_ckpt_load(const char* const* paths, int n_paths, const zero_plan* plan, int rank,
+                   float* master, float* m, float* v, int location, int64_t* step_out,
+                   void* staging, int64_t staging_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* CPU-offloaded optimizer (ZeRO-Offload)                                  */

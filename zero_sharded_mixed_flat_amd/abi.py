@@ -23,6 +23,7 @@ ZERO_EINVAL = -1
 ZERO_EALIAS = -2
 ZERO_EHIP = -3
 ZERO_ENOMEM = -4
+ZERO_EIO = -5
 ZERO_F16 = 1
 ZERO_BF16 = 2
 ZERO_MAX_RANKS = 1024
@@ -37,12 +38,17 @@ EXPORTED = (
     "zero_gather_params", "zero_last_error", "zero_version",
     "zero_quant_code_bytes", "zero_quant_scale_count", "zero_quantize_blocks", "zero_dequantize_blocks",
     "zero_gather_dequant", "zero_cpu_adam_step", "zero_offload_adam_step", "zero_cpu_isa", "zero_cpu_set_isa",
+    "zero_plan_reshard", "zero_ckpt_save", "zero_ckpt_load",
 )
 ZERO_QBLOCK = 256
 ZERO_CPU_SCALAR = 0
 ZERO_CPU_AVX2 = 1
 ZERO_CPU_AVX512 = 2
 ZERO_OFFLOAD_MIN_STAGING = 576
+ZERO_LOC_DEVICE = 0
+ZERO_LOC_HOST = 1
+ZERO_CKPT_BLOCK = 262144
+ZERO_CKPT_MIN_STAGING = 2 * 4 * ZERO_CKPT_BLOCK
 
 
 class ZeroError(RuntimeError):
@@ -54,6 +60,11 @@ class ZeroError(RuntimeError):
 class zero_segment(ctypes.Structure):
     _fields_ = [("tensor", ctypes.c_int64), ("tensor_off", ctypes.c_int64),
                 ("shard_off", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
+class zero_reshard_segment(ctypes.Structure):
+    _fields_ = [("old_rank", ctypes.c_int64), ("old_offset", ctypes.c_int64), ("new_offset", ctypes.c_int64),
+                ("len", ctypes.c_int64)]
 
 
 class zero_adam_hparams(ctypes.Structure):
@@ -100,6 +111,10 @@ _sig = {
                                 _P, _I, _I]),
     "zero_offload_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
                                     _P, _I64, _I, _P]),
+    "zero_plan_reshard": (_I, [_P, _P, _I, ctypes.POINTER(zero_reshard_segment), _I, ctypes.POINTER(_I)]),
+    "zero_ckpt_save": (_I, [ctypes.c_char_p, _P, _I, _I64, _P, _P, _P, _I, _P, _I64, _P]),
+    "zero_ckpt_load": (_I, [ctypes.POINTER(ctypes.c_char_p), _I, _P, _I, _P, _P, _P, _I, ctypes.POINTER(_I64), _P,
+                            _I64, _P]),
     "zero_cpu_isa": (_I, []),
     "zero_cpu_set_isa": (_I, [_I]),
     "zero_last_error": (ctypes.c_char_p, []),
@@ -281,6 +296,16 @@ class Plan:
         return [(s.tensor, s.tensor_off, s.shard_off, s.len) for s in out[:count.value]]
 
 
+def zero_plan_reshard(old_plan, new_plan, new_rank):
+    """Runs (old_rank, old_offset, new_offset, len) filling new_rank's shard from the old shards."""
+    count = _I()
+    _check(lib.zero_plan_reshard(old_plan.handle, new_plan.handle, int(new_rank), None, 0, ctypes.byref(count)))
+    out = (zero_reshard_segment * max(count.value, 1))()
+    _check(lib.zero_plan_reshard(old_plan.handle, new_plan.handle, int(new_rank), out, count.value,
+                                 ctypes.byref(count)))
+    return [(s.old_rank, s.old_offset, s.new_offset, s.len) for s in out[:count.value]]
+
+
 def zero_plan_create(unit_numels, nd, stage, align=8):
     return Plan(unit_numels, nd, stage, align)
 
@@ -458,3 +483,43 @@ def zero_offload_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, flag, pa
                                       ctypes.byref(hp), _ptr(coef), _ptr(flag), _ptr(param_out),
                                       _dtype(param_dtype), _ptr(staging), int(sb), int(n_threads),
                                       _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# sharded checkpoints
+# ---------------------------------------------------------------------------
+
+def _location(tensors):
+    devs = {t.is_cuda for t in tensors if t is not None and not isinstance(t, int)}
+    if len(devs) > 1:
+        raise ValueError("master, m and v must all be device tensors or all host tensors")
+    return ZERO_LOC_DEVICE if devs == {True} else ZERO_LOC_HOST
+
+
+def _check_state(plan, arrays, location):
+    n, _ = plan.rank(0)
+    for t, what in zip(arrays, ("master", "m", "v")):
+        (_need if location == ZERO_LOC_DEVICE else _need_host)(t, 4 * n, what)
+
+
+def zero_ckpt_save(path, plan, rank, step, master, m, v, staging, stream=None, location=None, staging_bytes=None):
+    loc = _location((master, m, v)) if location is None else location
+    _check_state(plan, (master, m, v), loc)
+    _need_host(staging, ZERO_CKPT_MIN_STAGING, "staging")
+    sb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    _check(lib.zero_ckpt_save(os.fsencode(path), plan.handle, int(rank), int(step), _ptr(master), _ptr(m), _ptr(v),
+                              int(loc), _ptr(staging), int(sb), _stream(stream) if loc == ZERO_LOC_DEVICE else None))
+
+
+def zero_ckpt_load(paths, plan, rank, master, m, v, staging, stream=None, location=None, staging_bytes=None):
+    """Restores rank's shard under ``plan`` from every old rank's file; returns the saved step."""
+    loc = _location((master, m, v)) if location is None else location
+    _check_state(plan, (master, m, v), loc)
+    _need_host(staging, ZERO_CKPT_MIN_STAGING, "staging")
+    sb = _nbytes(staging) if staging_bytes is None else staging_bytes
+    arr = (ctypes.c_char_p * len(paths))(*[os.fsencode(p) for p in paths])
+    step = _I64()
+    _check(lib.zero_ckpt_load(arr, len(paths), plan.handle, int(rank), _ptr(master), _ptr(m), _ptr(v), int(loc),
+                              ctypes.byref(step), _ptr(staging), int(sb),
+                              _stream(stream) if loc == ZERO_LOC_DEVICE else None))
+    return step.value

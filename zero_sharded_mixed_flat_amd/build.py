@@ -48,10 +48,13 @@ def build(verbose=True):
     objs = [plan_o]
     # Host AdamW (host code only, built by the host compiler): IEEE fp32 with no
     # contraction, so every instruction set gives the same bits.
+    host_flags = [f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__"]
     offload_o = os.path.join(objdir, "offload.o")
-    _run([_cxx(), *common, "-ffp-contract=off", f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__",
-          "-c", os.path.join(CSRC, "offload.cpp"), "-o", offload_o])
-    objs.append(offload_o)
+    _run([_cxx(), *common, "-ffp-contract=off", *host_flags, "-c", os.path.join(CSRC, "offload.cpp"),
+          "-o", offload_o])
+    ckpt_o = os.path.join(objdir, "ckpt.o")
+    _run([_cxx(), *common, *host_flags, "-c", os.path.join(CSRC, "ckpt.cpp"), "-o", ckpt_o])
+    objs += [offload_o, ckpt_o]
     for src in ("kernels.hip", "quant.hip"):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         _run([hipcc, *common, "-x", "hip", f"--offload-arch={ARCH}",

@@ -36,6 +36,16 @@ struct zero_plan {
 
 namespace zf {
 
+// Runs that fill `rank`'s shard under `neu` from the shards of `old` (same
+// parameter count), merged maximally, in new-shard order.
+void reshard_runs(const zero_plan& old, const zero_plan& neu, int rank, std::vector<zero_reshard_segment>& runs);
+
+int64_t plan_psi(const zero_plan& p);
+
+}  // namespace zf
+
+namespace zf {
+
 // Tiling of the streaming kernels.  A lane handles 4 consecutive elements (a
 // "quad") per access, so every load or store instruction of a wave touches
 // one contiguous span; a block owns a contiguous tile of quads.  The reduce

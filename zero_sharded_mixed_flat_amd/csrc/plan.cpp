@@ -36,6 +36,54 @@ int64_t partial_blocks(int64_t n) {
 
 }  // namespace zf
 
+namespace zf {
+
+// Maximal runs (old owner, old shard offset, new shard offset, length) that
+// fill `rank`'s shard under `neu` from the shards of `old`, in new-shard
+// order.  Both plans must partition the same number of parameters; the flat
+// parameter order (units concatenated) identifies a parameter.
+void reshard_runs(const zero_plan& old, const zero_plan& neu, int rank, std::vector<zero_reshard_segment>& runs) {
+    runs.clear();
+    const int r_new = neu.owners == 1 ? 0 : rank;
+    size_t k = 0;            // old unit holding flat position g
+    int64_t old_flat = 0;    // flat base of old unit k
+    int64_t new_flat = 0;    // flat base of the new unit
+    for (const auto& u : neu.units) {
+        const int64_t lo = std::min(int64_t(r_new) * u.slice_numel, u.numel);
+        const int64_t hi = std::min(int64_t(r_new + 1) * u.slice_numel, u.numel);
+        int64_t g = new_flat + lo;
+        const int64_t g_end = new_flat + hi;
+        int64_t j = u.shard_base + lo - int64_t(r_new) * u.slice_numel;
+        while (g < g_end) {
+            while (g >= old_flat + old.units[k].numel) old_flat += old.units[k++].numel;
+            const auto& ou = old.units[k];
+            const int64_t local = g - old_flat;
+            const int64_t r_old = old.owners == 1 ? 0 : local / ou.slice_numel;
+            const int64_t piece_end =
+                std::min({g_end, old_flat + ou.numel, old_flat + (r_old + 1) * ou.slice_numel});
+            const int64_t len = piece_end - g;
+            const int64_t k_off = ou.shard_base + local - r_old * ou.slice_numel;
+            zero_reshard_segment* last = runs.empty() ? nullptr : &runs.back();
+            if (last && last->old_rank == r_old && last->old_offset + last->len == k_off &&
+                last->new_offset + last->len == j)
+                last->len += len;
+            else
+                runs.push_back({r_old, k_off, j, len});
+            g += len;
+            j += len;
+        }
+        new_flat += u.numel;
+    }
+}
+
+int64_t plan_psi(const zero_plan& p) {
+    int64_t psi = 0;
+    for (const auto& u : p.units) psi += u.numel;
+    return psi;
+}
+
+}  // namespace zf
+
 extern "C" {
 
 const char* zero_last_error(void) { return zf::g_error.c_str(); }
@@ -184,6 +232,28 @@ int zero_plan_segments(const zero_plan* plan, const int64_t* tensor_numels, int 
         pos += len;
     }
     *count = written;
+    return zf::ok();
+}
+
+
+int zero_plan_reshard(const zero_plan* old_plan, const zero_plan* new_plan, int new_rank, zero_reshard_segment* out,
+                      int cap, int* count) {
+    if (old_plan == nullptr || new_plan == nullptr || count == nullptr)
+        return zf::fail(ZERO_EINVAL, "zero_plan_reshard: NULL argument");
+    if (cap < 0 || (cap > 0 && out == nullptr)) return zf::fail(ZERO_EINVAL, "zero_plan_reshard: bad capacity");
+    if (new_rank < 0 || new_rank >= new_plan->nd)
+        return zf::fail(ZERO_EINVAL, "zero_plan_reshard: rank out of range");
+    if (zf::plan_psi(*old_plan) != zf::plan_psi(*new_plan))
+        return zf::fail(ZERO_EINVAL, "zero_plan_reshard: the plans partition different parameter counts");
+    std::vector<zero_reshard_segment> runs;
+    try {
+        zf::reshard_runs(*old_plan, *new_plan, new_rank, runs);
+    } catch (const std::bad_alloc&) {
+        return zf::fail(ZERO_ENOMEM, "zero_plan_reshard: out of host memory");
+    }
+    if (runs.size() > size_t(INT32_MAX)) return zf::fail(ZERO_EINVAL, "zero_plan_reshard: too many runs");
+    for (size_t i = 0; i < runs.size() && i < size_t(cap); ++i) out[i] = runs[i];
+    *count = int(runs.size());
     return zf::ok();
 }
 
