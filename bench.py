@@ -232,6 +232,71 @@ def summarize_counters(fetch_csv, write_csv, phases, commands):
     return "\n".join(out) + "\n", entry
 
 
+CKPT_WORKLOAD = "gpt2_1p5b_nd16_z1"
+
+
+def checkpoint_bench(directory, name, seed):
+    """Save every rank's fp32 state (one file per rank, flushed to disk), then
+    restore the emulated rank's shard under the same partition and under half
+    as many ranks.  Throughput counts the restored rank's bytes."""
+    import shutil
+    import tempfile
+
+    import torch
+
+    from zero_sharded_mixed_flat_amd import abi, runner, workloads
+
+    w = workloads.get(name)
+    run = runner.RankStep(w, seed=seed)
+    run.step()
+    torch.cuda.synchronize()
+    n = run.n
+    state = (run.master[0], run.m[0], run.v[0])
+    per_rank = 3 * 4 * n
+    staging = torch.empty(64 << 20, dtype=torch.uint8, pin_memory=True)
+    work = tempfile.mkdtemp(prefix="zf-ckpt-", dir=directory)
+    try:
+        paths = [os.path.join(work, f"rank{r:04d}.zck") for r in range(w.nd)]
+        _log(f"checkpoint: saving {w.nd} x {per_rank / 1e9:.2f} GB to {work}")
+        save_s = []
+        for r, path in enumerate(paths):   # the other ranks' files hold this rank's arrays, same sizes
+            t0 = time.perf_counter()
+            abi.zero_ckpt_save(path, run.plan, r, run.t - 1, *state, staging)
+            save_s.append(time.perf_counter() - t0)
+        out = [torch.empty_like(state[0]) for _ in range(3)]
+        t0 = time.perf_counter()
+        abi.zero_ckpt_load(paths, run.plan, w.rank, *out, staging)
+        same_s = time.perf_counter() - t0
+        _, real = run.plan.rank(w.rank)
+        exact = all(torch.equal(a[:real], b[:real]) for a, b in zip(out, state))
+        half = abi.Plan(w.units, w.nd // 2, w.stage, w.align)
+        n_half, _ = half.rank(0)
+        out_half = [torch.empty(n_half, device="cuda") for _ in range(3)]
+        t0 = time.perf_counter()
+        abi.zero_ckpt_load(paths, half, w.rank // 2, *out_half, staging)
+        half_s = time.perf_counter() - t0
+        usage = shutil.disk_usage(work)
+    finally:
+        shutil.rmtree(work, ignore_errors=True)
+    result = {
+        "metric": "sharded checkpoint: save and restore of one rank's fp32 optimizer state",
+        "unit": "GB/s",
+        "workload": name,
+        "bytes_per_rank": per_rank,
+        "save_gbs_median": per_rank / sorted(save_s)[len(save_s) // 2] / 1e9,
+        "save_gbs_min": per_rank / max(save_s) / 1e9,
+        "restore_same_partition_gbs": per_rank / same_s / 1e9,
+        "restore_resharded_gbs": 3 * 4 * n_half / half_s / 1e9,
+        "reshard": f"{w.nd} -> {w.nd // 2} ranks, rank {w.rank // 2}",
+        "restore_bit_exact": bool(exact),
+        "durable": "fsync of each file and its directory before the save returns",
+        "storage_free_gb": usage.free / 1e9,
+        "data": "synthetic",
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +309,9 @@ def main():
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize FETCH_SIZE / WRITE_SIZE counter files, update profiles/traffic.json")
+    ap.add_argument("--checkpoint", metavar="DIR",
+                    help="time saving every rank's optimizer state to DIR and restoring one rank (same and "
+                         "halved rank count); prints one JSON line")
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the files being summarized")
     args = ap.parse_args()
@@ -287,6 +355,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.checkpoint:
+        return checkpoint_bench(args.checkpoint, args.workload or CKPT_WORKLOAD, args.seed)
     _log(f"bench: allocating {name}")
     run = runner.RankStep(w, seed=args.seed)
     torch.cuda.synchronize()

@@ -369,8 +369,9 @@ int zero_plan_reshard(const zero_plan* old_plan, const zero_plan* new_plan, int 
  * a resumable checkpoint holds the sharded optimizer state, not only the
  * weights).  Layout: a 4 KiB-aligned header (magic, version, Nd, stage,
  * align, rank, step, the unit sizes, one 64-bit checksum per 1 MiB block of
- * each array), then the three arrays.  The file is written as `path`.tmp and
- * renamed, so `path` never names a partial file.  `location`: ZERO_LOC_DEVICE
+ * each array), then the three arrays.  The file is written as `path`.tmp,
+ * flushed to stable storage and renamed (and the directory flushed), so
+ * `path` never names a partial file.  `location`: ZERO_LOC_DEVICE
  * (arrays in device memory, copied out through `staging` on `stream`) or
  * ZERO_LOC_HOST.  staging: pinned host memory, >= ZERO_CKPT_MIN_STAGING
  * bytes, 64-byte aligned.  Blocks until the file is complete.  Errors:

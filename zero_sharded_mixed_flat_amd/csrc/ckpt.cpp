@@ -331,6 +331,9 @@ int zero_ckpt_save(const char* path, const zero_plan* plan, int rank, int64_t st
         return abandon(fail(ZERO_EIO, std::string(fn) + ": writing '" + tmp + "': " + sys_reason()));
     if (n == 0 && ::ftruncate(out.fd, h.data_offset) != 0)
         return abandon(fail(ZERO_EIO, std::string(fn) + ": sizing '" + tmp + "': " + sys_reason()));
+    // On stable storage before it takes the final name, and the name itself after.
+    if (::fsync(out.fd) != 0)
+        return abandon(fail(ZERO_EIO, std::string(fn) + ": flushing '" + tmp + "': " + sys_reason()));
     if (::close(out.fd) != 0) {
         out.fd = -1;
         ::unlink(tmp.c_str());
@@ -341,6 +344,13 @@ int zero_ckpt_save(const char* path, const zero_plan* plan, int rank, int64_t st
         ::unlink(tmp.c_str());
         return fail(ZERO_EIO, std::string(fn) + ": renaming to '" + path + "': " + sys_reason());
     }
+    const std::string p(path);
+    const size_t slash = p.find_last_of('/');
+    const std::string dir = slash == std::string::npos ? "." : (slash == 0 ? "/" : p.substr(0, slash));
+    Fd d;
+    d.fd = ::open(dir.c_str(), O_RDONLY | O_DIRECTORY | O_CLOEXEC);
+    if (d.fd < 0 || ::fsync(d.fd) != 0)
+        return fail(ZERO_EIO, std::string(fn) + ": flushing directory '" + dir + "': " + sys_reason());
     return ok();
 }
 
