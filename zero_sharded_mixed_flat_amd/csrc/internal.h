@@ -63,10 +63,10 @@ namespace zf {
 #define ZF_PARTIAL_TILES 1
 #endif
 #ifndef ZF_ADAM_BLOCK
-#define ZF_ADAM_BLOCK 512
+#define ZF_ADAM_BLOCK 256
 #endif
 #ifndef ZF_ADAM_QUADS
-#define ZF_ADAM_QUADS 2
+#define ZF_ADAM_QUADS 4
 #endif
 constexpr int kReduceBlock = ZF_REDUCE_BLOCK;
 constexpr int kReduceQuadsPerLane = ZF_REDUCE_QUADS;

@@ -33,6 +33,7 @@ import torch
 from . import abi, synth
 
 OFFLOAD_CHUNK = 1 << 23          # values per staging slot of the offloaded update
+CONTRIB_ROW_ALIGN = 2048         # 16-bit elements: 4 KiB
 HOST_THREADS_MAX = 16
 
 TORCH16 = synth.TORCH_DTYPES
@@ -68,7 +69,11 @@ class RankStep:
             self.local = torch.empty((w.nd, self.full_numel), dtype=gdt, device=dev)
             self.fresh_gradients(step=0, tile_period=tile_period)
         else:
-            self.contrib_block = torch.empty((w.nd, n), dtype=gdt, device=dev)
+            # Rows start on 4 KiB boundaries, as separate (peer) buffers would:
+            # a row stride of 2n bytes alone can leave every wave-wide access
+            # straddling one more 128-byte line than it needs.
+            row = -(-n // CONTRIB_ROW_ALIGN) * CONTRIB_ROW_ALIGN
+            self.contrib_block = torch.empty((w.nd, row), dtype=gdt, device=dev)[:, :n]
             for r in range(w.nd):
                 synth.normal_(self.contrib_block[r], w.grad_std * w.loss_scale, seed, 100 + r)
                 synth.outliers_(self.contrib_block[r], w.outlier_frac, w.outlier_mult, seed, 100 + r)
