@@ -16,6 +16,8 @@ from oracle import rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import abi
 
+from tolerance import param16_ok, state_ok
+
 HPARAMS = {
     "adam": AdamHparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0),
     "adamw": AdamHparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1),
@@ -54,17 +56,6 @@ def _run(g, p, m, v, gdt, pdt, hp, t, coef, threads, skip=False):
     return tp.numpy(), tm.numpy(), tv.numpy(), out.numpy().view(np.uint16)
 
 
-def _state_ok(got, ref, what):
-    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
-    bad = np.flatnonzero(np.abs(got - ref) > 1e-9 + 1e-6 * np.abs(ref))
-    assert bad.size == 0, f"{what}: {bad.size} out of tolerance, e.g. {got[bad[:3]]} vs {ref[bad[:3]]}"
-
-
-def _ulp_ok(got, ref, what):
-    d = np.abs(rounding.ordered16(got) - rounding.ordered16(ref))
-    assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} values more than 1 ulp apart"
-
-
 @pytest.mark.parametrize("gdt, pdt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16"), ("bf16", "f16")])
 @pytest.mark.parametrize("hp_name", sorted(HPARAMS))
 @pytest.mark.parametrize("n", [1, 15, 16, 17, 1000, 100_003])
@@ -75,8 +66,8 @@ def test_matches_oracle(gdt, pdt, hp_name, n):
         got = _run(g, p, m, v, gdt, pdt, hp, t, coef, threads=3)
         ref = step.adam_update(p, m, v, g, gdt, hp, t, np.float32(coef), pdt)
         for k, what in enumerate(("master", "m", "v")):
-            _state_ok(got[k], ref[k], f"{what} t={t}")
-        _ulp_ok(got[3], ref[3], f"param t={t}")
+            state_ok(got[k], ref[k], f"{what} t={t}")
+        param16_ok(got[3], ref[3], pdt, f"param t={t}")
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

@@ -15,6 +15,7 @@ import torch
 from oracle import rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth
+from tolerance import param16_ok, state_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -47,17 +48,6 @@ def _inputs(n, gdt, seed):
     return g, p, m, v
 
 
-def _state_ok(got, ref, what):
-    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
-    bad = np.flatnonzero(np.abs(got - ref) > 1e-9 + 1e-6 * np.abs(ref))
-    assert bad.size == 0, f"{what}: {bad.size} out of tolerance"
-
-
-def _ulp_ok(got, ref, what):
-    d = np.abs(rounding.ordered16(got) - rounding.ordered16(ref))
-    assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} values more than 1 ulp apart"
-
-
 def _offload(abi, g, p, m, v, gdt, pdt, t, coef, flag, staging_bytes, threads=4, declared=None):
     n = g.size
     hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
@@ -81,8 +71,8 @@ def test_offload_matches_oracle_and_host_adam(abi, gdt, pdt, n, staging):
     got = _offload(abi, g, p, m, v, gdt, pdt, 3, float(coef), 0, staging)
     ref = step.adam_update(p, m, v, g, gdt, HP, 3, coef, pdt)
     for k, what in enumerate(("master", "m", "v")):
-        _state_ok(got[k], ref[k], what)
-    _ulp_ok(got[3], ref[3], "param")
+        state_ok(got[k], ref[k], what)
+    param16_ok(got[3], ref[3], pdt, "param")
     # the same update by the host AdamW called directly: identical bits
     hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
     out = torch.zeros(n, dtype=torch.int16)

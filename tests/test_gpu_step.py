@@ -17,6 +17,7 @@ import torch
 from oracle import partition, quant, rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth, workloads
+from tolerance import param16_ok, state_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -42,18 +43,6 @@ def _hp(w):
                        inv_loss_scale=w.inv_loss_scale, max_norm=w.max_norm)
 
 
-def _state_ok(got, ref, what):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    bad = np.flatnonzero(np.abs(got - ref) > 1e-9 + 1e-6 * np.abs(ref))
-    assert bad.size == 0, f"{what}: {bad.size} out of tolerance, e.g. gpu {got[bad[:3]]} oracle {ref[bad[:3]]}"
-
-
-def _ulp_ok(got, ref, what):
-    d = np.abs(rounding.ordered16(got) - rounding.ordered16(ref))
-    assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} params more than 1 ulp apart"
-
-
 def test_tiny_all_ranks_three_steps(runner):
     w = workloads.get("tiny_nd4_z2")
     _note(f"tiny workload {w.name}")
@@ -76,8 +65,8 @@ def test_tiny_all_ranks_three_steps(runner):
         assert ref["norm"] < w.max_norm and run.coef.item() == 1.0   # no clipping at this scale
         for i in range(w.nd):
             for got, exp, name in zip((run.master[i], run.m[i], run.v[i]), ref["states"][i], "pmv"):
-                _state_ok(_np32(got), exp, f"step {t} owner {i} {name}")
-        _ulp_ok(synth.bits(run.full), ref["full"], f"step {t} full buffer")
+                state_ok(_np32(got), exp, f"step {t} owner {i} {name}")
+        param16_ok(synth.bits(run.full), ref["full"], w.param_dtype, f"step {t} full buffer")
         states = ref["states"]
 
 
@@ -143,10 +132,10 @@ def test_shrunk_layouts_two_steps(runner, name):
             assert np.array_equal(synth.bits(run.reduced[0]), reduced)
         assert run.norm.item() == pytest.approx(norm, rel=1e-5)
         assert float(coef) < 1.0                        # clipping is active
-        _state_ok(_np32(run.master[0]), p, f"t={t} master")
-        _state_ok(_np32(run.m[0]), m, f"t={t} m")
-        _state_ok(_np32(run.v[0]), v, f"t={t} v")
-        _ulp_ok(synth.bits(run.param_out(0)), bits, f"t={t} param")
+        state_ok(_np32(run.master[0]), p, f"t={t} master")
+        state_ok(_np32(run.m[0]), m, f"t={t} m")
+        state_ok(_np32(run.v[0]), v, f"t={t} v")
+        param16_ok(synth.bits(run.param_out(0)), bits, w.param_dtype, f"t={t} param")
         state = (p, m, v)
         if others is not None:
             others[w.rank] = bits
@@ -155,7 +144,7 @@ def test_shrunk_layouts_two_steps(runner, name):
             # other owners' slices are synthetic inputs: bit for bit
             assert np.array_equal(got[~own], expect[~own]), f"t={t} gathered slices of other owners"
             if w.gather_bits == 16:
-                _ulp_ok(got[own], expect[own], f"t={t} own gathered slice")
+                param16_ok(got[own], expect[own], w.param_dtype, f"t={t} own gathered slice")
             else:
                 # the own 16-bit shard may be one ulp from the oracle's, which can
                 # move a block's scale: within one quantisation step of the oracle

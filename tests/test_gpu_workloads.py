@@ -7,9 +7,9 @@ pre-reduced gradient) is tiled with a ragged period P, so the reduced
 gradient is tiled too and its exact sum of squares is
 (n // P) * S(one period) + S(first n % P elements).  Everything else
 (reduced gradient bit for bit, master/m/v, 16-bit parameters, gathered
-buffer) is compared on sampled chunks -- first, last, random and unit
-boundaries -- computed one by one by the oracle from the actual device
-inputs copied back before the step.
+buffer) is compared on sampled chunks of 2^20 elements -- first, last, 16
+random ones and unit boundaries -- computed one by one by the oracle from the
+actual device inputs copied back before the step.
 """
 
 import gc
@@ -21,11 +21,13 @@ import torch
 from oracle import partition, quant, rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth, workloads
+from tolerance import param16_ok, state_ok
 
 pytestmark = pytest.mark.gpu
 
 PERIOD = (1 << 20) + 37
-CHUNK = 1 << 16
+CHUNK = 1 << 20
+N_RANDOM_CHUNKS = 16
 
 
 @pytest.fixture
@@ -47,23 +49,11 @@ def _hp(w):
                        inv_loss_scale=w.inv_loss_scale, max_norm=w.max_norm)
 
 
-def _state_ok(got, ref, what):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    bad = np.flatnonzero(np.abs(got - ref) > 1e-9 + 1e-6 * np.abs(ref))
-    assert bad.size == 0, f"{what}: {bad.size} out of tolerance, e.g. gpu {got[bad[:3]]} oracle {ref[bad[:3]]}"
-
-
-def _ulp_ok(got, ref, what):
-    d = np.abs(rounding.ordered16(got) - rounding.ordered16(ref))
-    assert d.size == 0 or d.max() <= 1, f"{what}: {int((d > 1).sum())} params more than 1 ulp apart"
-
-
 def _offsets(n, extra=(), seed=0, align=1):
     rng = np.random.default_rng(seed)
     last = max(0, n - CHUNK) // align * align
     offs = {0, last}
-    offs.update(int(x) // align * align for x in rng.integers(0, max(1, n - CHUNK), size=6))
+    offs.update(int(x) // align * align for x in rng.integers(0, max(1, n - CHUNK), size=N_RANDOM_CHUNKS))
     offs.update(min(max(0, int(x)), last) // align * align for x in extra)
     return sorted(offs)
 
@@ -186,10 +176,10 @@ def test_full_size_step(runner, name):
         else:
             reduced = grad
         p, m, v, bits = step.adam_update(p0, m0, v0, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
-        _state_ok(run.master[0, o:o + CHUNK].cpu().numpy(), p, f"master @ {o}")
-        _state_ok(run.m[0, o:o + CHUNK].cpu().numpy(), m, f"m @ {o}")
-        _state_ok(run.v[0, o:o + CHUNK].cpu().numpy(), v, f"v @ {o}")
-        _ulp_ok(synth.bits(run.param_out(0)[o:o + CHUNK]), bits, f"param @ {o}")
+        state_ok(run.master[0, o:o + CHUNK].cpu().numpy(), p, f"master @ {o}")
+        state_ok(run.m[0, o:o + CHUNK].cpu().numpy(), m, f"m @ {o}")
+        state_ok(run.v[0, o:o + CHUNK].cpu().numpy(), v, f"v @ {o}")
+        param16_ok(synth.bits(run.param_out(0)[o:o + CHUNK]), bits, w.param_dtype, f"param @ {o}")
         if run.codes is not None:
             _check_quantised_gather(run, plan, w, o, others, bits)
         elif others is not None:
