@@ -62,8 +62,19 @@ def measured_traffic(workload, kernel):
     return entry.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
+CPU_THREADS_MAX = 16
+
+
 def cpu_baseline(run, budget_s=12.0):
-    """Time the CPU oracle on a bounded sample of this workload's own inputs."""
+    """Time the CPU oracle, as it stands, on a bounded sample of this workload's inputs.
+
+    One thread per host core (at most 16), each running the oracle's step on
+    its own chunk of the shard (chunks spread over the shard) until the time
+    budget is spent; numpy releases the interpreter lock inside its array
+    operations, so the threads run in parallel.
+    """
+    import threading
+
     import numpy as np
 
     from oracle import partition
@@ -74,83 +85,67 @@ def cpu_baseline(run, budget_s=12.0):
 
     w = run.w
     hp = AdamHparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.inv_loss_scale, w.max_norm)
-    chunk = min(1 << 21, run.n)
-    # Inputs: the first `chunk` elements of each contribution and of the state.
-    if w.pre_reduced:
-        grad = synth.bits(run.grad[:chunk])
-        contribs = None
-    else:
-        contribs = [synth.bits(c[:chunk]) for c in run.contribs(0)]
-    master = run.master[0, :chunk].cpu().numpy()
-    m = run.m[0, :chunk].cpu().numpy()
-    v = run.v[0, :chunk].cpu().numpy()
-    elems, reps = 0, 0
-    parity = None
-    t0 = time.perf_counter()
-    while True:
-        if contribs is not None:
-            reduced, _ = ostep.reduce_shard(contribs, w.grad_dtype)
+    threads = max(1, min(CPU_THREADS_MAX, len(os.sched_getaffinity(0))))
+    chunk = min(1 << 20, run.n)
+    offsets = [min(run.n - chunk, (k * run.n) // threads) // 8 * 8 for k in range(threads)]
+
+    def inputs(o):
+        if w.pre_reduced:
+            contribs, grad = None, synth.bits(run.grad[o:o + chunk])
         else:
-            reduced = grad
-        norm = ostep.norm_from_sumsq(ostep.sumsq_exact(reduced, w.grad_dtype, w.inv_loss_scale))
-        coef = ostep.clip_coef(norm, w.max_norm)
-        _, _, _, param = ostep.adam_update(master, m, v, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
-        if w.gather_bits != 16:
-            # quantise the owned chunk once, dequantise every rank's codes into the sample layout
-            codes, scales = oquant.quantize(param, w.param_dtype, w.gather_bits)
-            full = np.empty(chunk * w.nd, np.uint16)
-            for r in range(w.nd):
-                full[r * chunk:(r + 1) * chunk] = oquant.dequantize(codes, scales, w.param_dtype)
-        elif w.gather_per_unit:
-            # the gather, on a one-unit sample layout whose slices are `chunk` long
-            sample_plan = partition.make_plan([chunk * w.nd], w.nd, 3, 1)
-            ostep.gather(sample_plan, [reduced] * w.nd, np.empty(chunk * w.nd, np.uint16))
-        elems += chunk
-        reps += 1
-        if parity is None and contribs is not None:
-            parity = bool(np.array_equal(reduced, synth.bits(run.reduced[0, :chunk])))
-        if time.perf_counter() - t0 >= budget_s:
-            break
+            contribs, grad = [synth.bits(c[o:o + chunk]) for c in run.contribs(0)], None
+        state = tuple(t[0, o:o + chunk].cpu().numpy().copy() for t in (run.master, run.m, run.v))
+        return contribs, grad, state
+
+    samples = [inputs(o) for o in offsets]
+    counts = [0] * threads
+    first_reduced = [None]
+    stop = time.perf_counter() + budget_s
+
+    def work(k):
+        contribs, grad, (master, m, v) = samples[k]
+        while True:
+            reduced = grad if contribs is None else ostep.reduce_shard(contribs, w.grad_dtype)[0]
+            norm = ostep.norm_from_sumsq(ostep.sumsq_exact(reduced, w.grad_dtype, w.inv_loss_scale))
+            coef = ostep.clip_coef(norm, w.max_norm)
+            _, _, _, param = ostep.adam_update(master, m, v, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
+            if w.gather_bits != 16:
+                # quantise the owned chunk once, dequantise every rank's codes into the sample layout
+                codes, scales = oquant.quantize(param, w.param_dtype, w.gather_bits)
+                full = np.empty(chunk * w.nd, np.uint16)
+                for r in range(w.nd):
+                    full[r * chunk:(r + 1) * chunk] = oquant.dequantize(codes, scales, w.param_dtype)
+            elif w.gather_per_unit:
+                # the gather, on a one-unit sample layout whose slices are `chunk` long
+                sample_plan = partition.make_plan([chunk * w.nd], w.nd, 3, 1)
+                ostep.gather(sample_plan, [reduced] * w.nd, np.empty(chunk * w.nd, np.uint16))
+            if k == 0 and first_reduced[0] is None:
+                first_reduced[0] = reduced
+            counts[k] += chunk
+            if time.perf_counter() >= stop:
+                return
+
+    t0 = time.perf_counter()
+    pool = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
     dt = time.perf_counter() - t0
+    parity = None
+    if not w.pre_reduced:
+        o = offsets[0]
+        parity = bool(np.array_equal(first_reduced[0], synth.bits(run.reduced[0, o:o + chunk])))
     return {
-        "value": elems / dt,
+        "value": sum(counts) / dt,
         "unit": "params/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps} x {chunk} owned elements of this workload's inputs (reduce over {w.nd} ranks, "
-                  f"exact norm, AdamW{_gather_label(w)}), single-threaded numpy",
+        "sample": f"{threads} threads, each on its own {chunk}-element chunk of this workload's inputs "
+                  f"({sum(counts) // chunk} chunk steps: reduce over {w.nd} ranks, exact norm, "
+                  f"AdamW{_gather_label(w)}), numpy",
         "seconds": round(dt, 3),
     }, parity
-
-
-def host_copy_gbs(threads, nbytes=1 << 31):
-    """Host memory copy bandwidth (read + write bytes per second / 1e9) with ``threads`` threads."""
-    import torch
-    saved = torch.get_num_threads()
-    torch.set_num_threads(threads)
-    try:
-        a = torch.ones(nbytes // 4, dtype=torch.float32)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        best = float("inf")
-        for _ in range(3):
-            t0 = time.perf_counter()
-            b.copy_(a)
-            best = min(best, time.perf_counter() - t0)
-        return 2 * nbytes / best / 1e9
-    finally:
-        torch.set_num_threads(saved)
-
-
-def cpu_model():
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return None
 
 
 def _gather_label(w):
