@@ -72,6 +72,27 @@ def test_quantize_dequantize(abi, bits, dtype, n):
     assert np.all(codes.cpu().numpy()[abi.zero_quant_code_bytes(n, bits):] == 0)   # nothing past the end
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n", [5, 1000, 65543, 1_000_003])
+def test_quantize_general_path(abi, bits, dtype, n):
+    # x only 8-byte aligned (and INT8 codes only 4-byte aligned): the per-block
+    # kernel instead of the 1024-element-span one; the same codes and scales.
+    _note(f"quantize general path bits={bits} dtype={dtype} n={n}")
+    rng = np.random.default_rng(n + bits + 1)
+    x = _params(rng, n, dtype)
+    ref_codes, ref_scales = quant.quantize(x, dtype, bits)
+    buf = torch.zeros(n + 8, dtype=TORCH16[dtype], device="cuda")
+    buf[4:4 + n].copy_(_dev16(x, dtype))
+    cbuf = torch.zeros(abi.zero_quant_code_bytes(n, bits) + 16, dtype=torch.uint8, device="cuda")
+    codes = cbuf[4:] if bits == 8 else cbuf
+    scales = torch.zeros(abi.zero_quant_scale_count(n), dtype=torch.float32, device="cuda")
+    abi.zero_quantize_blocks(buf[4:4 + n], dtype, n, bits, codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    assert np.array_equal(_host_codes(codes, bits, n), ref_codes)
+
+
 def test_zero_blocks_and_ties(abi):
     x = np.concatenate([rounding.narrow(np.zeros(256, np.float32), "f16"),
                         rounding.narrow(np.array([63.5, -127.0, 2.5, -3.5] * 64, np.float32), "f16")])

@@ -10,7 +10,8 @@
 // 2 bytes written instead of 2 + 2.  All streams are HBM-bound; nothing is a
 // contraction.
 //
-//   quantize_kernel        16-bit shard -> codes + fp32 scales
+//   quantize_span_kernel   16-bit shard -> codes + fp32 scales (aligned inputs)
+//   quantize_kernel        the same for any 8-byte-aligned input
 //   dequantize_kernel      codes + scales -> 16-bit
 //   gather_dequant_kernel  every owner's codes of one unit -> the unit's
 //                          16-bit slices of the full buffer
@@ -99,6 +100,92 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t*
                     if (e < n) {
                         const int hi = e + 1 < n ? (q[2 * p + 1] & 0xf) : 0;
                         codes[e / 2] = static_cast<uint8_t>((q[2 * p] & 0xf) | (hi << 4));
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Aligned inputs: a wave takes 1024-element spans.  Lane l loads 8 elements
+// (16 bytes) at span offsets 8l and 512 + 8l, so each load instruction reads
+// one contiguous KiB; lanes 0-31 / 32-63 of a load hold one 256-element block,
+// whose absmax is a 32-lane shuffle reduction.  Codes go out 8 per lane per
+// store (8 bytes of INT8 or 4 bytes of INT4), again contiguous per
+// instruction.  x must be 16-byte aligned, INT8 codes 8-byte aligned.
+constexpr int kQSpan = 1024;
+constexpr int kQSpansPerWave = 2;
+
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* codes, int64_t e, const int (&q)[8]) {
+    if constexpr (BITS == 8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            lo |= uint32_t(q[k] & 0xff) << (8 * k);
+            hi |= uint32_t(q[4 + k] & 0xff) << (8 * k);
+        }
+        st_stream(reinterpret_cast<u2*>(codes + e), u2{lo, hi});
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w |= uint32_t(q[k] & 0xf) << (4 * k);
+        st_stream(reinterpret_cast<uint32_t*>(codes + e / 2), w);
+    }
+}
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(kQuantThreads) void quantize_span_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                      int64_t nblocks, uint8_t* __restrict__ codes,
+                                                                      float* __restrict__ scales) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t span0 = (int64_t(blockIdx.x) * kQuantWaves + wave) * kQSpansPerWave;
+    float v[kQSpansPerWave][2][8];
+#pragma unroll
+    for (int j = 0; j < kQSpansPerWave; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t e0 = (span0 + j) * kQSpan + 512 * h + 8 * lane;
+            if (e0 + 8 <= n) {
+                const u4 w = ld_stream(reinterpret_cast<const u4*>(x + e0));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    v[j][h][2 * k] = widen<DT>(w[k] & 0xffffu);
+                    v[j][h][2 * k + 1] = widen<DT>(w[k] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[j][h][k] = e0 + k < n ? widen<DT>(x[e0 + k]) : 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kQSpansPerWave; ++j) {
+        if ((span0 + j) * kQSpan >= n) break;  // uniform over the wave
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t blk = (span0 + j) * (kQSpan / kQBlock) + 2 * h + (lane >> 5);
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[j][h][k]));
+            for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+            const float scale = amax / qmax_of<BITS>();
+            int q[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) q[k] = code_of<BITS>(v[j][h][k], scale);
+            if ((lane & 31) == 0 && blk < nblocks) scales[blk] = scale;
+            const int64_t e0 = (span0 + j) * kQSpan + 512 * h + 8 * lane;
+            if (e0 + 8 <= n) {
+                store_codes8<BITS>(codes, e0, q);
+            } else if constexpr (BITS == 8) {
+                for (int k = 0; k < 8; ++k)
+                    if (e0 + k < n) codes[e0 + k] = static_cast<uint8_t>(q[k] & 0xff);
+            } else {
+                for (int k = 0; k < 8; k += 2) {
+                    const int64_t e = e0 + k;
+                    if (e < n) {
+                        const int hi = e + 1 < n ? (q[k + 1] & 0xf) : 0;
+                        codes[e / 2] = static_cast<uint8_t>((q[k] & 0xf) | (hi << 4));
                     }
                 }
             }
@@ -253,8 +340,16 @@ inline bool valid_bits(int bits) { return bits == 8 || bits == 4; }
 inline int64_t code_bytes(int64_t n, int bits) { return bits == 8 ? n : (n + 1) / 2; }
 
 template <int DT>
-hipError_t launch_quantize(int bits, dim3 grid, hipStream_t s, const uint16_t* x, int64_t n, int64_t nb,
+hipError_t launch_quantize(int bits, bool spans, hipStream_t s, const uint16_t* x, int64_t n, int64_t nb,
                            uint8_t* codes, float* scales) {
+    if (spans) {
+        const int64_t waves = ceil_div(ceil_div(n, int64_t(kQSpan)), int64_t(kQSpansPerWave));
+        const dim3 grid{unsigned(ceil_div(waves, int64_t(kQuantWaves)))};
+        if (bits == 8)
+            return launch(quantize_span_kernel<DT, 8>, grid, dim3(kQuantThreads), s, x, n, nb, codes, scales);
+        return launch(quantize_span_kernel<DT, 4>, grid, dim3(kQuantThreads), s, x, n, nb, codes, scales);
+    }
+    const dim3 grid{unsigned(ceil_div(nb, int64_t(kQuantWaves) * kQuantBlocksPerWave))};
     if (bits == 8) return launch(quantize_kernel<DT, 8>, grid, dim3(kQuantThreads), s, x, n, nb, codes, scales);
     return launch(quantize_kernel<DT, 4>, grid, dim3(kQuantThreads), s, x, n, nb, codes, scales);
 }
@@ -315,11 +410,11 @@ int zero_quantize_blocks(const void* x, int dtype, int64_t n, int bits, void* co
     if (overlaps(x, 2 * n, codes, cb) || overlaps(x, 2 * n, scales, 4 * nb) || overlaps(codes, cb, scales, 4 * nb))
         return fail(ZERO_EALIAS, std::string(fn) + ": x, codes and scales must not overlap");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid{unsigned(ceil_div(nb, int64_t(kQuantWaves) * kQuantBlocksPerWave))};
     const uint16_t* x16 = static_cast<const uint16_t*>(x);
     uint8_t* c8 = static_cast<uint8_t*>(codes);
-    const hipError_t e = dtype == ZERO_F16 ? launch_quantize<ZERO_F16>(bits, grid, s, x16, n, nb, c8, scales)
-                                           : launch_quantize<ZERO_BF16>(bits, grid, s, x16, n, nb, c8, scales);
+    const bool spans = (addr(x) & 15) == 0 && (bits == 4 || (addr(codes) & 7) == 0);
+    const hipError_t e = dtype == ZERO_F16 ? launch_quantize<ZERO_F16>(bits, spans, s, x16, n, nb, c8, scales)
+                                           : launch_quantize<ZERO_BF16>(bits, spans, s, x16, n, nb, c8, scales);
     return hip_status(e, fn);
 }
 
