@@ -28,8 +28,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "zero_sharded_mixed_flat_amd", "csrc", f)
-                  for f in ("kernels.hip", "quant.hip", "device.h", "internal.h")]
+CSRC = os.path.join(ROOT, "zero_sharded_mixed_flat_amd", "csrc")
+QUANT_KERNELS = ("quantize", "dequantize", "gather_dequant")
 COPY_ELEMS = 1 << 31            # the reference copy: 4 GiB of 16-bit values
 COPY_BYTES_EACH_WAY = 2 * COPY_ELEMS
 
@@ -38,10 +38,12 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
+    """Hash of the sources a kernel is built from (its file and the shared headers)."""
+    own = "quant.hip" if kernel.startswith(QUANT_KERNELS) else "kernels.hip"
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in (own, "device.h", "internal.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -49,17 +51,18 @@ def kernel_source_hash():
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of one kernel of a workload from committed rocprofv3 counters.
 
-    Only used when the counters were taken from the current kernel sources.
+    Only used while the kernel's sources hash as they did when the counters
+    were taken.
     """
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get(workload)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+    entry = data.get(workload, {}).get("kernels", {}).get(kernel)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
-    return entry.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
+    return entry.get("bytes_per_launch")
 
 
 CPU_THREADS_MAX = 16
@@ -160,16 +163,32 @@ def _short(name):
 
 
 def summarize_trace(stats_csv, command):
-    """Markdown table of a rocprofv3 --stats kernel summary (kernels of this library first)."""
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: its kernel
+    statistics (this library's kernels first), then the same dispatches from
+    the per-dispatch trace grouped by kernel and grid size, which separates
+    launches of one kernel that do different work."""
     import csv
+    from collections import defaultdict
     rows = list(csv.DictReader(open(stats_csv)))
     ours = [r for r in rows if "zf::" in r["Name"]]
     other = [r for r in rows if "zf::" not in r["Name"]]
     out = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
+           "rocprofv3 kernel statistics:", "",
            "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in ours + other[:4]:
         out.append(f"| `{_short(r['Name'])[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    if trace_csv != stats_csv and os.path.exists(trace_csv):
+        groups = defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            if "zf::" in r["Kernel_Name"]:
+                groups[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out += ["", "This library's dispatches by grid size (from the per-dispatch trace of the same run):", "",
+                "| kernel | grid (threads) | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
+        for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| `{name}` | {grid} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
     return "\n".join(out) + "\n"
 
 
@@ -221,9 +240,9 @@ def summarize_counters(fetch_csv, write_csv, phases, commands):
                    f"| {alg if alg is None else f'{alg:.4g}'} | {ratio} |")
         if phase and prefix not in kernels:
             kernels[prefix] = {"kernel": k[0], "grid": k[1], "bytes_per_launch": rb + wb, "bytes_read": rb,
-                               "bytes_written": wb, "algorithmic_bytes_per_launch": alg}
-    entry = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_scale": fetch_scale,
-             "write_scale": write_scale, "kernels": kernels}
+                               "bytes_written": wb, "algorithmic_bytes_per_launch": alg,
+                               "kernel_source_sha256_16": kernel_source_hash(prefix)}
+    entry = {"fetch_scale": fetch_scale, "write_scale": write_scale, "kernels": kernels}
     return "\n".join(out) + "\n", entry
 
 

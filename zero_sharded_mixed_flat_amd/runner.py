@@ -293,7 +293,8 @@ def phase_model(w, plan):
         out["adam"] = {"kernel": "adam_kernel", "launches": owners, "bytes_per_launch": 28 * n}
     if w.gather_bits != 16:
         code = abi.zero_quant_code_bytes(n, w.gather_bits) + 4 * abi.zero_quant_scale_count(n)
-        out["quantize"] = {"kernel": "quantize_kernel", "launches": owners, "bytes_per_launch": 2 * n + code}
+        # shards are 16-byte aligned, so the span kernel runs
+        out["quantize"] = {"kernel": "quantize_span_kernel", "launches": owners, "bytes_per_launch": 2 * n + code}
         out["gather"] = {"kernel": "gather_dequant_kernel", "launches": n_units,
                          "bytes_per_launch": (code + 2 * n) * w.nd / n_units}
     elif w.gather_per_unit:
