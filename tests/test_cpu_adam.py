@@ -16,7 +16,7 @@ from oracle import rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import abi
 
-from tolerance import param16_ok, state_ok
+from tolerance import AdamTrack, adam_ok
 
 HPARAMS = {
     "adam": AdamHparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0),
@@ -65,9 +65,27 @@ def test_matches_oracle(gdt, pdt, hp_name, n):
     for t, coef in ((1, 1.0), (7, 0.37)):
         got = _run(g, p, m, v, gdt, pdt, hp, t, coef, threads=3)
         ref = step.adam_update(p, m, v, g, gdt, hp, t, np.float32(coef), pdt)
-        for k, what in enumerate(("master", "m", "v")):
-            state_ok(got[k], ref[k], f"{what} t={t}")
-        param16_ok(got[3], ref[3], pdt, f"param t={t}")
+        adam_ok(got, ref, (p, m, v), g, gdt, hp, t, np.float32(coef), pdt, f"t={t}")
+
+
+@pytest.mark.parametrize("gdt, pdt", [("f16", "f16"), ("bf16", "bf16")])
+def test_five_steps_each_side_on_its_own_state(gdt, pdt):
+    # The host AdamW (the GPU kernel's operation sequence) and the oracle each
+    # step from their own previous state; the carried bound must hold at every step.
+    hp = HPARAMS["adamw"]
+    n = 200_003
+    rng = np.random.default_rng(12)
+    _, p, m, v = _inputs(n, gdt, hp, 12)
+    host = (p, m, v)
+    track = AdamTrack()
+    for t in range(1, 6):
+        g = rounding.narrow((rng.standard_normal(n) * 1e-3).astype(np.float32), gdt)
+        coef = np.float32(0.9)
+        got = _run(g, *host, gdt, pdt, hp, t, coef, threads=4)
+        ref = step.adam_update(p, m, v, g, gdt, hp, t, coef, pdt)
+        track.check(got, ref, (p, m, v), g, gdt, hp, t, coef, pdt, f"t={t}")
+        host = got[:3]
+        p, m, v = ref[:3]
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

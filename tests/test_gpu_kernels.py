@@ -13,7 +13,7 @@ import torch
 
 from oracle import partition, rounding, step
 from oracle.step import AdamHparams
-from tolerance import param16_ok, state_ok
+from tolerance import adam_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -337,10 +337,8 @@ def test_adam(abi, gdt, pdt, hpname, n, offset, poffset):
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     abi.zero_adam_step(d_master, d_m, d_v, d_g, gdt, n, _hp(abi, hp, t), d_coef, flag, d_p, pdt)
     torch.cuda.synchronize()
-    state_ok(d_master.cpu().numpy(), p_ref, "master")
-    state_ok(d_m.cpu().numpy(), m_ref, "m")
-    state_ok(d_v.cpu().numpy(), v_ref, "v")
-    param16_ok(_bits(d_p), bits_ref, pdt, "param")
+    got = (d_master.cpu().numpy(), d_m.cpu().numpy(), d_v.cpu().numpy(), _bits(d_p))
+    adam_ok(got, (p_ref, m_ref, v_ref, bits_ref), (master, m, v), g, gdt, hp, t, coef, pdt, "adam")
 
 
 def test_adam_skips_when_flagged(abi):

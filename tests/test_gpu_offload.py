@@ -15,7 +15,7 @@ import torch
 from oracle import rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth
-from tolerance import param16_ok, state_ok
+from tolerance import adam_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -70,9 +70,7 @@ def test_offload_matches_oracle_and_host_adam(abi, gdt, pdt, n, staging):
     coef = np.float32(0.6)
     got = _offload(abi, g, p, m, v, gdt, pdt, 3, float(coef), 0, staging)
     ref = step.adam_update(p, m, v, g, gdt, HP, 3, coef, pdt)
-    for k, what in enumerate(("master", "m", "v")):
-        state_ok(got[k], ref[k], what)
-    param16_ok(got[3], ref[3], pdt, "param")
+    adam_ok(got, ref, (p, m, v), g, gdt, HP, 3, coef, pdt, "offload")
     # the same update by the host AdamW called directly: identical bits
     hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
     out = torch.zeros(n, dtype=torch.int16)

@@ -21,7 +21,7 @@ import torch
 from oracle import partition, quant, rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth, workloads
-from tolerance import param16_ok, state_ok
+from tolerance import adam_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -176,10 +176,9 @@ def test_full_size_step(runner, name):
         else:
             reduced = grad
         p, m, v, bits = step.adam_update(p0, m0, v0, reduced, w.grad_dtype, hp, 1, coef, w.param_dtype)
-        state_ok(run.master[0, o:o + CHUNK].cpu().numpy(), p, f"master @ {o}")
-        state_ok(run.m[0, o:o + CHUNK].cpu().numpy(), m, f"m @ {o}")
-        state_ok(run.v[0, o:o + CHUNK].cpu().numpy(), v, f"v @ {o}")
-        param16_ok(synth.bits(run.param_out(0)[o:o + CHUNK]), bits, w.param_dtype, f"param @ {o}")
+        got = tuple(t[0, o:o + CHUNK].cpu().numpy() for t in (run.master, run.m, run.v))
+        got += (synth.bits(run.param_out(0)[o:o + CHUNK]),)
+        adam_ok(got, (p, m, v, bits), (p0, m0, v0), reduced, w.grad_dtype, hp, 1, coef, w.param_dtype, f"@ {o}")
         if run.codes is not None:
             _check_quantised_gather(run, plan, w, o, others, bits)
         elif others is not None:

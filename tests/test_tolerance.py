@@ -1,13 +1,17 @@
-"""The derived 16-bit parameter tolerance accepts what the fp32 master's
-tolerance allows and nothing more: two ulps apart at ordinary magnitudes
-fails; near zero, a difference within the master's absolute tolerance
-passes even when it spans several 16-bit ulps."""
+"""The derived AdamW tolerances accept the fp32 arithmetic's rounding and
+nothing grossly more: a 16-bit parameter two ulps off fails at ordinary
+magnitudes; the bounds scale with the operands of each update (so a small
+result after cancellation gets an operand-sized bound), and a planted error
+of a few hundred fp32 ulps in an ordinary element fails."""
 
 import numpy as np
 import pytest
 
-from oracle import rounding
-from tolerance import param16_ok
+from oracle import rounding, step
+from oracle.step import AdamHparams
+from tolerance import U32, adam_bounds, adam_ok, param16_ok
+
+HP = AdamHparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
 
 def _b(vals, dt):
@@ -15,7 +19,7 @@ def _b(vals, dt):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_one_ulp_passes_two_fail_at_ordinary_magnitude(dt):
+def test_param_one_ulp_passes_two_fail_at_ordinary_magnitude(dt):
     x = _b([0.02, -0.013, 1.5], dt)
     param16_ok(x, x, dt, "equal")
     param16_ok(x + np.uint16(1), x, dt, "one ulp")
@@ -23,14 +27,47 @@ def test_one_ulp_passes_two_fail_at_ordinary_magnitude(dt):
         param16_ok(x + np.uint16(2), x, dt, "two ulps")
 
 
-def test_near_zero_within_the_master_tolerance():
-    # bf16 values of 3e-10 and 1e-10 differ by many ulps but by 2e-10 < 1e-9
+def test_param_within_the_master_bound_near_zero():
     got, ref = _b([3e-10], "bf16"), _b([1e-10], "bf16")
-    param16_ok(got, ref, "bf16", "cancellation")
+    param16_ok(got, ref, "bf16", "cancellation", master_bound=np.array([2.5e-10]))
     with pytest.raises(AssertionError):
-        param16_ok(_b([3e-9], "bf16"), ref, "bf16", "beyond the absolute tolerance")
-    # across zero in fp16: -0 against the smallest subnormal is one ulp in value
-    # (two encodings apart) and passes; -1 against +1 subnormal is two and fails
+        param16_ok(got, ref, "bf16", "no master bound")
+    # fp16 across zero: -0 against the smallest subnormal is one ulp in value
     param16_ok(np.uint16([0x8000]), np.uint16([0x0001]), "f16", "-0 vs the smallest subnormal")
     with pytest.raises(AssertionError):
         param16_ok(np.uint16([0x8001]), np.uint16([0x0001]), "f16", "opposite subnormals")
+
+
+def test_bounds_scale_with_the_operands():
+    # ordinary element: the bound on p is a few dozen ulps of |p|
+    g = _b([1e-4, 1e-4], "bf16")
+    p = np.float32([0.02, 0.003])
+    m = np.float32([1e-5, 1e-4])
+    v = np.float32([1e-8, 1e-16])                # the second: tiny v, a large step that nearly cancels p
+    bp, bm, bv = adam_bounds(p, m, v, g, "bf16", HP, 1, np.float32(1.0))
+    g0 = float(rounding.widen(g, "bf16")[0])
+    a = (0.9 * 1e-5 + 0.1 * g0) / 0.1 / (np.sqrt((0.95 * 1e-8 + 0.05 * g0 * g0) / 0.05) + 1e-8)
+    assert bp[0] == pytest.approx(24 * U32 * (0.02 + 3e-4 * a + 3e-4 * 0.1 * 0.02), rel=1e-3)
+    ref = step.adam_update(p, m, v, g, "bf16", HP, 1, np.float32(1.0), "bf16")
+    step_size = abs(float(p[1]) - float(ref[0][1]))
+    assert step_size > 1e-3                      # the update is large
+    assert bp[1] > 24 * U32 * step_size          # and the bound follows it, not |p'|
+    assert bm[0] <= 8 * U32 * 1e-5 and bv[0] <= 16 * U32 * 1e-8
+
+
+def test_planted_error_fails():
+    rng = np.random.default_rng(0)
+    n = 1000
+    g = _b(rng.standard_normal(n) * 1e-4, "bf16")
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-5).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * 1e-8).astype(np.float32)
+    coef = np.float32(0.7)
+    ref = step.adam_update(p, m, v, g, "bf16", HP, 2, coef, "bf16")
+    adam_ok(ref, ref, (p, m, v), g, "bf16", HP, 2, coef, "bf16", "identical")
+    k = int(np.argmax(np.abs(p)))
+    for which in range(3):
+        bad = [a.copy() for a in ref]
+        bad[which][k] = np.float32(bad[which][k] * (1 + 300 * U32))
+        with pytest.raises(AssertionError):
+            adam_ok(tuple(bad), ref, (p, m, v), g, "bf16", HP, 2, coef, "bf16", f"planted in output {which}")
