@@ -392,8 +392,11 @@ def main():
     stream = torch.cuda.current_stream()
     phases = ["reduce", "norm", "adam", "quantize", "gather"]
     acc = {p: 0.0 for p in phases}
+    step_ms = []
     for _ in range(args.steps):
-        ev = {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for p in phases}
+        ev = {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for p in phases + ["step"]}
+        ev["step"][0].record(stream)
         run.flag.zero_()
         if not w.pre_reduced:
             ev["reduce"][0].record(stream)
@@ -413,8 +416,10 @@ def main():
             ev["gather"][0].record(stream)
             run.gather_all()
             ev["gather"][1].record(stream)
+        ev["step"][1].record(stream)
         run.t += 1
         torch.cuda.synchronize()
+        step_ms.append(ev["step"][0].elapsed_time(ev["step"][1]))
         for p in phases:
             if (p == "reduce" and w.pre_reduced or p == "gather" and run.shards is None
                     or p == "quantize" and run.codes is None):
@@ -494,6 +499,8 @@ def main():
         "hbm_frac_of_peak": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": alg_bytes,
         "kernel_ms": {k: round(v, 6) for k, v in kern_ms.items() if v > 0},
+        "step_ms_events": {"median": sorted(step_ms)[len(step_ms) // 2], "min": min(step_ms), "max": max(step_ms),
+                           "steps": len(step_ms)},
         "copy_ceiling": {"kernel": "gather_kernel as a plain 4 GiB -> 4 GiB copy", "gbs": copy_gbs,
                          "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
                          "step_frac_of_copy": step_gbs / copy_gbs,
