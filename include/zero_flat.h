@@ -14,7 +14,10 @@
  *   then holds a message for the calling thread.  Every argument is checked
  *   BEFORE anything is enqueued: on error nothing has been launched and no
  *   output has been touched (the pages' validate-then-act rule: L18 notes §5.1
- *   and §5.4; fail explicitly, never partially: 026 notes §五).
+ *   and §5.4; fail explicitly, never partially: 026 notes §五).  The only
+ *   exceptions are failures that can first appear part-way through a call
+ *   that streams data (a checkpoint block found corrupt, a copy refused by
+ *   the runtime); those functions say which outputs are then unusable.
  * - Device buffers are owned by the caller (allocated with any allocator,
  *   e.g. PyTorch).  The library allocates no device memory; kernels that need
  *   scratch use the caller's workspace (zero_workspace_bytes).
@@ -393,7 +396,10 @@ int zero_ckpt_save(const char* path, const zero_plan* plan, int rank, int64_t st
  * *step_out: the saved step count.  staging as for zero_ckpt_save.  Blocks
  * until the state is in place.  Errors: ZERO_EIO (missing, short or corrupt
  * file, naming its rank and path), ZERO_EINVAL (mismatched files or plans,
- * arguments), ZERO_EHIP.
+ * arguments), ZERO_EHIP.  Missing, foreign, truncated and mismatched files
+ * are found before any output is written; a corrupt block or a failed read
+ * or copy is found while copying, and master, m and v are then partly
+ * written and must not be used.
  */
 int zero_ckpt_load(const char* const* paths, int n_paths, const zero_plan* plan, int rank,
                    float* master, float* m, float* v, int location, int64_t* step_out,
@@ -445,7 +451,9 @@ int zero_cpu_adam_step(float* master, float* m, float* v, const void* grad, int 
  * ZERO_OFFLOAD_MIN_STAGING bytes; (staging_bytes - 64) / 8 values per chunk.
  * Blocks the calling thread until the last parameters have reached the
  * device (the stream is synchronised).  Errors: ZERO_EINVAL (arguments, or a
- * non-positive clip multiplier on the device), ZERO_EALIAS, ZERO_EHIP.
+ * non-positive clip multiplier on the device), ZERO_EALIAS, ZERO_EHIP.  The
+ * clip multiplier is checked before any state changes; a copy refused by the
+ * runtime part-way leaves master, m, v and the parameters partly updated.
  */
 int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_dev,
                            int grad_dtype, int64_t n, const zero_adam_hparams* hp,
