@@ -323,6 +323,8 @@ def main():
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize FETCH_SIZE / WRITE_SIZE counter files, update profiles/traffic.json")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step as a HIP graph after the warmup and time its replays")
     ap.add_argument("--checkpoint", metavar="DIR",
                     help="time saving every rank's optimizer state to DIR and restoring one rank (same and "
                          "halved rank count); prints one JSON line")
@@ -379,11 +381,17 @@ def main():
     for _ in range(args.warmup):
         run.step()
     torch.cuda.synchronize()
+    step_fn = run.step
+    if args.graph:
+        run.capture()
+        run.replay()                     # one untimed replay
+        torch.cuda.synchronize()
+        step_fn = run.replay
 
     # Whole steps, wall clock bracketed by device synchronisation.
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run.step()
+        step_fn()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
@@ -494,6 +502,7 @@ def main():
             "workload": name, "psi": w.psi, "nd": w.nd, "zero_stage": w.stage, "rank": w.rank,
             "emulated_owners": len(run.owners), "shard_numel": run.n, "grad_dtype": w.grad_dtype,
             "param_dtype": w.param_dtype, "state_dtype": "f32", "parallelism": "one rank's share, 1 GPU",
+            "hip_graph": bool(args.graph),
         },
         "hbm_gbs": step_gbs,
         "hbm_frac_of_peak": step_gbs / HBM_PEAK_GBS,

@@ -257,6 +257,30 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
                    int64_t n, const zero_adam_hparams* hp, const float* coef_dev,
                    const int32_t* flag, void* param_out, int param_dtype, void* stream);
 
+/* The fp32 scalars of one AdamW step, as zero_adam_step derives them from
+ * zero_adam_hparams: 1 - beta formed in fp32, bias corrections f32(1 - beta^t)
+ * from fp64 and their fp32 reciprocals. */
+typedef struct {
+    float lr, beta1, beta2, one_minus_beta1, one_minus_beta2, eps, weight_decay, inv_loss_scale;
+    float inv_bias_corr1, inv_bias_corr2;
+} zero_adam_consts;
+
+/* Fills *out (host) from hp, with zero_adam_step's checks.  Errors: ZERO_EINVAL. */
+int zero_adam_consts_fill(const zero_adam_hparams* hp, zero_adam_consts* out);
+
+/*
+ * zero_adam_step_consts -- zero_adam_step with its scalars read from device
+ * memory (consts_dev: a zero_adam_consts filled by zero_adam_consts_fill and
+ * copied to the device, 4-byte aligned), so a launch captured in a HIP graph
+ * replays with the step count, learning rate and bias corrections the caller
+ * writes there before each replay.  The same kernel and the same bits as
+ * zero_adam_step for the same scalars.  The values in consts_dev are not
+ * validated at launch.  Other arguments and errors as zero_adam_step.
+ */
+int zero_adam_step_consts(float* master, float* m, float* v, const void* grad, int grad_dtype,
+                          int64_t n, const zero_adam_consts* consts_dev, const float* coef_dev,
+                          const int32_t* flag, void* param_out, int param_dtype, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* a4: gather of 16-bit shards into the full parameter buffer              */
 /* ---------------------------------------------------------------------- */

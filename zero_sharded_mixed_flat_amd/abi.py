@@ -38,7 +38,7 @@ EXPORTED = (
     "zero_gather_params", "zero_last_error", "zero_version",
     "zero_quant_code_bytes", "zero_quant_scale_count", "zero_quantize_blocks", "zero_dequantize_blocks",
     "zero_gather_dequant", "zero_cpu_adam_step", "zero_offload_adam_step", "zero_cpu_isa", "zero_cpu_set_isa",
-    "zero_plan_reshard", "zero_ckpt_save", "zero_ckpt_load",
+    "zero_plan_reshard", "zero_ckpt_save", "zero_ckpt_load", "zero_adam_consts_fill", "zero_adam_step_consts",
 )
 ZERO_QBLOCK = 256
 ZERO_CPU_SCALAR = 0
@@ -73,6 +73,12 @@ class zero_adam_hparams(ctypes.Structure):
                 ("inv_loss_scale", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
+class zero_adam_consts(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_float) for name in (
+        "lr", "beta1", "beta2", "one_minus_beta1", "one_minus_beta2", "eps", "weight_decay", "inv_loss_scale",
+        "inv_bias_corr1", "inv_bias_corr2")]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m zero_sharded_mixed_flat_amd.build`")
 
@@ -102,6 +108,8 @@ _sig = {
     "zero_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
                             _P]),
     "zero_gather_params": (_I, [_P, ctypes.POINTER(_P), _I, _I, _I, _P, _P, _I64, _P]),
+    "zero_adam_consts_fill": (_I, [ctypes.POINTER(zero_adam_hparams), ctypes.POINTER(zero_adam_consts)]),
+    "zero_adam_step_consts": (_I, [_P, _P, _P, _P, _I, _I64, _P, _P, _P, _P, _I, _P]),
     "zero_quant_code_bytes": (_I64, [_I64, _I]),
     "zero_quant_scale_count": (_I64, [_I64]),
     "zero_quantize_blocks": (_I, [_P, _I, _I64, _I, _P, _P, _P]),
@@ -374,6 +382,24 @@ def zero_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, flag, param_out,
     _check(lib.zero_adam_step(_ptr(master), _ptr(m), _ptr(v), _ptr(grad), _dtype(grad_dtype), int(n),
                               ctypes.byref(hp), _ptr(coef), _ptr(flag), _ptr(param_out),
                               _dtype(param_dtype), _stream(stream)))
+
+
+def zero_adam_consts_fill(hp):
+    """The fp32 scalars zero_adam_step derives from hp, as a zero_adam_consts (host)."""
+    out = zero_adam_consts()
+    _check(lib.zero_adam_consts_fill(ctypes.byref(hp), ctypes.byref(out)))
+    return out
+
+
+def zero_adam_step_consts(master, m, v, grad, grad_dtype, n, consts_dev, coef, flag, param_out, param_dtype,
+                          stream=None):
+    for t, b, what in ((master, 4 * n, "master"), (m, 4 * n, "m"), (v, 4 * n, "v"),
+                       (grad, 2 * n, "grad"), (param_out, 2 * n, "param_out"), (coef, 4, "coef"),
+                       (flag, 4, "flag"), (consts_dev, ctypes.sizeof(zero_adam_consts), "consts_dev")):
+        _need(t, b, what)
+    _check(lib.zero_adam_step_consts(_ptr(master), _ptr(m), _ptr(v), _ptr(grad), _dtype(grad_dtype), int(n),
+                                     _ptr(consts_dev), _ptr(coef), _ptr(flag), _ptr(param_out), _dtype(param_dtype),
+                                     _stream(stream)))
 
 
 def zero_gather_params(plan, shards, unit_begin, unit_end, dtype, full, workspace=None, stream=None,

@@ -309,16 +309,19 @@ struct AdamConsts {
 
 // Block b covers quads [b*kAdamTileQuads, (b+1)*kAdamTileQuads) of the body (or
 // elements [b*kAdamTileElems, ...) without `vec`).
-template <int GDT, int PDT>
+// DEV: the scalars come from device memory (c_dev) instead of the kernel
+// arguments, so a captured graph can replay the launch with new ones.
+template <int GDT, int PDT, bool DEV>
 __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ master,
                                                       float* __restrict__ m,
                                                       float* __restrict__ v,
                                                       const uint16_t* __restrict__ grad, Span sp,
-                                                      AdamConsts c,
+                                                      AdamConsts c_arg, const AdamConsts* __restrict__ c_dev,
                                                       const float* __restrict__ coef_dev,
                                                       const int32_t* __restrict__ flag,
                                                       uint16_t* __restrict__ param) {
     if (*flag != 0) return;  // a skipped step writes nothing
+    const AdamConsts c = DEV ? *c_dev : c_arg;
     const float gs = c.inv_s * *coef_dev;
 
     auto update = [&](float& p, float& mm, float& vv, uint32_t gb) -> uint32_t {
@@ -472,15 +475,96 @@ hipError_t launch_reduce(int nd, dim3 grid, hipStream_t s, const Ptrs64& tab,
 #undef ZF_REDUCE
 }
 
+template <int GDT, int PDT>
+hipError_t launch_adam_p(const AdamConsts* c_dev, dim3 grid, hipStream_t s, float* master, float* m, float* v,
+                         const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
+                         const int32_t* flag, uint16_t* param) {
+    if (c_dev != nullptr)
+        return launch(adam_kernel<GDT, PDT, true>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c, c_dev,
+                      coef, flag, param);
+    return launch(adam_kernel<GDT, PDT, false>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c,
+                  static_cast<const AdamConsts*>(nullptr), coef, flag, param);
+}
+
 template <int GDT>
-hipError_t launch_adam(int pdt, dim3 grid, hipStream_t s, float* master, float* m, float* v,
-                       const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
+hipError_t launch_adam(int pdt, const AdamConsts* c_dev, dim3 grid, hipStream_t s, float* master, float* m,
+                       float* v, const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
                        const int32_t* flag, uint16_t* param) {
     if (pdt == ZERO_F16)
-        return launch(adam_kernel<GDT, ZERO_F16>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c,
-                      coef, flag, param);
-    return launch(adam_kernel<GDT, ZERO_BF16>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c, coef,
-                  flag, param);
+        return launch_adam_p<GDT, ZERO_F16>(c_dev, grid, s, master, m, v, grad, sp, c, coef, flag, param);
+    return launch_adam_p<GDT, ZERO_BF16>(c_dev, grid, s, master, m, v, grad, sp, c, coef, flag, param);
+}
+
+static_assert(sizeof(zero_adam_consts) == sizeof(AdamConsts), "zero_adam_consts mirrors AdamConsts");
+
+// The fp32 scalars of an AdamW step from its hyperparameters (validated).
+int adam_consts(const char* fn, const zero_adam_hparams* hp, AdamConsts* c) {
+    if (hp == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": hp is NULL");
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
+        !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(ZERO_EINVAL, std::string(fn) + ": hyperparameters must be finite, betas in [0, 1)");
+    if (hp->step < 1) return fail(ZERO_EINVAL, std::string(fn) + ": step must be >= 1");
+    if (!pow2_positive(hp->inv_loss_scale))
+        return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
+    c->lr = hp->lr;
+    c->b1 = hp->beta1;
+    c->b2 = hp->beta2;
+    c->omb1 = float(1.0 - double(hp->beta1));
+    c->omb2 = float(1.0 - double(hp->beta2));
+    c->eps = hp->eps;
+    c->wd = hp->weight_decay;
+    c->inv_s = hp->inv_loss_scale;
+    const float bc1 = float(1.0 - std::pow(double(hp->beta1), double(hp->step)));
+    const float bc2 = float(1.0 - std::pow(double(hp->beta2), double(hp->step)));
+    if (!(bc1 > 0.0f) || !(bc2 > 0.0f)) return fail(ZERO_EINVAL, std::string(fn) + ": bias correction is zero");
+    c->inv_bc1 = float(1.0 / double(bc1));
+    c->inv_bc2 = float(1.0 / double(bc2));
+    return ZERO_OK;
+}
+
+// Checks the buffers of an AdamW launch and enqueues it (scalars by value,
+// or from c_dev when it is not NULL).
+int adam_enqueue(const char* fn, float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
+                 const AdamConsts& c, const AdamConsts* c_dev, const float* coef_dev, const int32_t* flag,
+                 void* param_out, int param_dtype, void* stream) {
+    if (n < 0) return fail(ZERO_EINVAL, std::string(fn) + ": n < 0");
+    if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
+        return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
+    if (coef_dev == nullptr || (addr(coef_dev) & 3) || flag == nullptr || (addr(flag) & 3))
+        return fail(ZERO_EINVAL, std::string(fn) + ": coef_dev or flag NULL or misaligned");
+    if (n > 0) {
+        if (!master || !m || !v || !grad || !param_out)
+            return fail(ZERO_EINVAL, std::string(fn) + ": NULL buffer");
+        if ((addr(master) | addr(m) | addr(v)) & 3)
+            return fail(ZERO_EINVAL, std::string(fn) + ": fp32 buffers must be 4-byte aligned");
+        if ((addr(grad) | addr(param_out)) & 1)
+            return fail(ZERO_EINVAL, std::string(fn) + ": 16-bit buffers must be 2-byte aligned");
+        const void* outs[4] = {master, m, v, param_out};
+        const int64_t ob[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+        for (int i = 0; i < 4; ++i) {
+            for (int j = i + 1; j < 4; ++j)
+                if (overlaps(outs[i], ob[i], outs[j], ob[j]))
+                    return fail(ZERO_EALIAS, std::string(fn) + ": master, m, v and param_out must not overlap");
+            if (overlaps(outs[i], ob[i], grad, 2 * n) || overlaps(outs[i], ob[i], coef_dev, 4) ||
+                overlaps(outs[i], ob[i], flag, 4) ||
+                (c_dev != nullptr && overlaps(outs[i], ob[i], c_dev, int64_t(sizeof(AdamConsts)))))
+                return fail(ZERO_EALIAS, std::string(fn) + ": an output overlaps grad, coef, flag or the scalars");
+        }
+    }
+    if (n == 0) return ok();
+    const void* p16[2] = {grad, param_out};
+    const void* p32[3] = {master, m, v};
+    const Span sp = make_span(n, p16, 2, p32, 3);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t blocks = sp.vec ? std::max<int64_t>(1, ceil_div(sp.nq, kAdamTileQuads)) : ceil_div(n, kAdamTileElems);
+    const dim3 grid{unsigned(blocks)};
+    const uint16_t* g16 = static_cast<const uint16_t*>(grad);
+    uint16_t* p16o = static_cast<uint16_t*>(param_out);
+    const hipError_t e =
+        grad_dtype == ZERO_F16
+            ? launch_adam<ZERO_F16>(param_dtype, c_dev, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o)
+            : launch_adam<ZERO_BF16>(param_dtype, c_dev, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o);
+    return hip_status(e, fn);
 }
 
 }  // namespace
@@ -627,66 +711,31 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
                    const zero_adam_hparams* hp, const float* coef_dev, const int32_t* flag,
                    void* param_out, int param_dtype, void* stream) {
     const char* fn = "zero_adam_step";
-    if (n < 0) return fail(ZERO_EINVAL, std::string(fn) + ": n < 0");
-    if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
-        return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
-    if (hp == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": hp is NULL");
-    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
-        !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(ZERO_EINVAL, std::string(fn) + ": hyperparameters must be finite, betas in [0, 1)");
-    if (hp->step < 1) return fail(ZERO_EINVAL, std::string(fn) + ": step must be >= 1");
-    if (!pow2_positive(hp->inv_loss_scale))
-        return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
-    if (coef_dev == nullptr || (addr(coef_dev) & 3) || flag == nullptr || (addr(flag) & 3))
-        return fail(ZERO_EINVAL, std::string(fn) + ": coef_dev or flag NULL or misaligned");
-    if (n > 0) {
-        if (!master || !m || !v || !grad || !param_out)
-            return fail(ZERO_EINVAL, std::string(fn) + ": NULL buffer");
-        if ((addr(master) | addr(m) | addr(v)) & 3)
-            return fail(ZERO_EINVAL, std::string(fn) + ": fp32 buffers must be 4-byte aligned");
-        if ((addr(grad) | addr(param_out)) & 1)
-            return fail(ZERO_EINVAL, std::string(fn) + ": 16-bit buffers must be 2-byte aligned");
-        const void* outs[4] = {master, m, v, param_out};
-        const int64_t ob[4] = {4 * n, 4 * n, 4 * n, 2 * n};
-        for (int i = 0; i < 4; ++i) {
-            for (int j = i + 1; j < 4; ++j)
-                if (overlaps(outs[i], ob[i], outs[j], ob[j]))
-                    return fail(ZERO_EALIAS, std::string(fn) + ": master, m, v and param_out must not overlap");
-            if (overlaps(outs[i], ob[i], grad, 2 * n) || overlaps(outs[i], ob[i], coef_dev, 4) ||
-                overlaps(outs[i], ob[i], flag, 4))
-                return fail(ZERO_EALIAS, std::string(fn) + ": an output overlaps grad, coef or flag");
-        }
-    }
-    if (n == 0) return ok();
-
     AdamConsts c;
-    c.lr = hp->lr;
-    c.b1 = hp->beta1;
-    c.b2 = hp->beta2;
-    c.omb1 = float(1.0 - double(hp->beta1));
-    c.omb2 = float(1.0 - double(hp->beta2));
-    c.eps = hp->eps;
-    c.wd = hp->weight_decay;
-    c.inv_s = hp->inv_loss_scale;
-    const float bc1 = float(1.0 - std::pow(double(hp->beta1), double(hp->step)));
-    const float bc2 = float(1.0 - std::pow(double(hp->beta2), double(hp->step)));
-    if (!(bc1 > 0.0f) || !(bc2 > 0.0f)) return fail(ZERO_EINVAL, std::string(fn) + ": bias correction is zero");
-    c.inv_bc1 = float(1.0 / double(bc1));
-    c.inv_bc2 = float(1.0 / double(bc2));
+    if (int rc = adam_consts(fn, hp, &c)) return rc;
+    return adam_enqueue(fn, master, m, v, grad, grad_dtype, n, c, nullptr, coef_dev, flag, param_out, param_dtype,
+                        stream);
+}
 
-    const void* p16[2] = {grad, param_out};
-    const void* p32[3] = {master, m, v};
-    const Span sp = make_span(n, p16, 2, p32, 3);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t blocks = sp.vec ? std::max<int64_t>(1, ceil_div(sp.nq, kAdamTileQuads)) : ceil_div(n, kAdamTileElems);
-    const dim3 grid{unsigned(blocks)};
-    const uint16_t* g16 = static_cast<const uint16_t*>(grad);
-    uint16_t* p16o = static_cast<uint16_t*>(param_out);
-    const hipError_t e =
-        grad_dtype == ZERO_F16
-            ? launch_adam<ZERO_F16>(param_dtype, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o)
-            : launch_adam<ZERO_BF16>(param_dtype, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o);
-    return hip_status(e, fn);
+int zero_adam_consts_fill(const zero_adam_hparams* hp, zero_adam_consts* out) {
+    const char* fn = "zero_adam_consts_fill";
+    if (out == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": out is NULL");
+    AdamConsts c;
+    if (int rc = adam_consts(fn, hp, &c)) return rc;
+    std::memcpy(out, &c, sizeof(c));
+    return ok();
+}
+
+int zero_adam_step_consts(float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
+                          const zero_adam_consts* consts_dev, const float* coef_dev, const int32_t* flag,
+                          void* param_out, int param_dtype, void* stream) {
+    const char* fn = "zero_adam_step_consts";
+    if (consts_dev == nullptr || (addr(consts_dev) & 3))
+        return fail(ZERO_EINVAL, std::string(fn) + ": consts_dev NULL or not 4-byte aligned");
+    const AdamConsts unused{};
+    return adam_enqueue(fn, master, m, v, grad, grad_dtype, n, unused,
+                        reinterpret_cast<const AdamConsts*>(consts_dev), coef_dev, flag, param_out, param_dtype,
+                        stream);
 }
 
 int zero_gather_params(const zero_plan* plan, const void* const* shards, int unit_begin, int unit_end,

@@ -210,11 +210,15 @@ class RankStep:
         abi.zero_grad_norm(grad, self.n, w.grad_dtype, w.inv_loss_scale, self.ws, self.n_sets, None, 0,
                            w.max_norm, self.flag, self.norm, self.coef, stream)
 
-    def adam_all(self, stream=None):
+    def adam_all(self, stream=None, consts_dev=None):
         w = self.w
         hp = self.hparams()
         for i in range(len(self.owners)):
-            if w.offload:
+            if consts_dev is not None:
+                abi.zero_adam_step_consts(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype,
+                                          self.n, consts_dev, self.coef, self.flag, self.param_out(i),
+                                          w.param_dtype, stream)
+            elif w.offload:
                 abi.zero_offload_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype,
                                            self.n, hp, self.coef, self.flag, self.param_out(i), w.param_dtype,
                                            self.staging, self.host_threads, stream)
@@ -242,17 +246,44 @@ class RankStep:
         for u in range(self.n_units):
             self.gather_unit(u, stream)
 
-    def step(self, stream=None):
-        """Enqueue one whole step; returns without synchronising."""
+    def _enqueue(self, stream=None, consts_dev=None):
         self.flag.zero_()
         if not self.w.pre_reduced:
             self.reduce_all(stream)
         self.norm_all(stream)
-        self.adam_all(stream)
+        self.adam_all(stream, consts_dev)
         if self.codes is not None:
             self.quantize_all(stream)
         if self.shards is not None:
             self.gather_all(stream)
+
+    def step(self, stream=None):
+        """Enqueue one whole step; returns without synchronising."""
+        self._enqueue(stream)
+        self.t += 1
+
+    # -- the step as a HIP graph -----------------------------------------------
+
+    def capture(self):
+        """Capture one whole step as a HIP graph (no host work inside a step).
+
+        AdamW then reads its scalars (step count, bias corrections) from a
+        device buffer that replay() refreshes before each launch of the graph.
+        """
+        if self.w.offload:
+            raise ValueError("the offloaded update runs on the host and cannot be captured")
+        self.consts_dev = torch.zeros(len(abi.zero_adam_consts._fields_), dtype=torch.float32, device=self.device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._enqueue(consts_dev=self.consts_dev)
+
+    def replay(self):
+        """Launch the captured step for the current step count; returns without synchronising."""
+        c = abi.zero_adam_consts_fill(self.hparams())
+        # from pageable host memory: the runtime stages the 40 bytes before the
+        # call returns, so consecutive replays never see each other's values
+        self.consts_dev.copy_(torch.frombuffer(bytearray(c), dtype=torch.float32))
+        self.graph.replay()
         self.t += 1
 
     # -- accounting ------------------------------------------------------------
