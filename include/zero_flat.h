@@ -24,7 +24,11 @@
  * - Device work is enqueued asynchronously on `stream` (a hipStream_t passed
  *   as void*; NULL = the null stream) on the current HIP device.  Results are
  *   valid once the stream reaches that point.  Calls are re-entrant; calls
- *   that share a workspace or flag must be ordered on one stream.
+ *   that share a workspace or flag must be ordered on one stream.  The step's
+ *   calls record no memset and no host synchronisation, so they can be
+ *   captured in a HIP graph, except the reduce and the gathers with more than
+ *   64 ranks (their pointer table is copied from host memory; they return
+ *   ZERO_EINVAL on a capturing stream).
  * - 16-bit data: ZERO_F16 (IEEE binary16) or ZERO_BF16.  Optimizer state is
  *   always fp32.  Element counts are int64; n = 0 is a no-op (where a device
  *   output is defined for n = 0, e.g. the norm, it is still written).

@@ -71,3 +71,23 @@ def test_offload_cannot_be_captured(runner):
     w = dataclasses.replace(workloads.get("llama3_8b_nd8_z2_offload"), psi=8 * 1000, units=(8 * 1000,))
     with pytest.raises(ValueError):
         runner.RankStep(w, seed=1).capture()
+
+
+def test_more_than_64_ranks_refuse_capture(runner):
+    # Their pointer table is copied from host memory: captured, the copy would
+    # keep a host address, so the call refuses before enqueueing anything.
+    from zero_sharded_mixed_flat_amd import abi
+    n, nd = 4096, 65
+    contribs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(nd)]
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(abi.zero_workspace_bytes(n, 1), dtype=torch.uint8, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(abi.ZeroError) as e:
+        with torch.cuda.graph(g):
+            abi.zero_reduce_shard(contribs, n, "bf16", 1.0, out, ws, 0, flag)
+    assert e.value.code == abi.ZERO_EINVAL and "captured" in str(e.value)
+    # eagerly, the same call works
+    abi.zero_reduce_shard(contribs, n, "bf16", 1.0, out, ws, 0, flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0 and not out.float().abs().sum().item()

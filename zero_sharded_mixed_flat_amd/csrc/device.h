@@ -178,6 +178,20 @@ inline int hip_status(hipError_t e, const char* where) {
     return ok();
 }
 
+// More than 64 rank pointers reach the kernels through a table copied from
+// host memory into the workspace.  A captured graph would keep that copy's
+// host address, not the pointers, so such calls refuse to be captured.
+inline int refuse_capture(hipStream_t s, const char* fn) {
+    hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(s, &status);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (status != hipStreamCaptureStatusNone)
+        return fail(ZERO_EINVAL, std::string(fn) +
+                                     ": more than 64 ranks cannot be captured in a graph (the pointer table is "
+                                     "copied from host memory)");
+    return ZERO_OK;
+}
+
 // Launches `kernel` and returns the status of THIS launch.  hipGetLastError()
 // is not used: it also reports earlier failures of other libraries' calls on
 // this thread.  The arguments are converted to the kernel's parameter types.

@@ -622,6 +622,7 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
     } else {
         // The runtime stages a pageable source before returning, so `ptrs`
         // may go out of scope once the call is back.
+        if (int rc = refuse_capture(s, fn)) return rc;
         dtab = static_cast<const uint16_t* const*>(workspace);
         const hipError_t e = hipMemcpyAsync(workspace, ptrs.data(), sizeof(void*) * nd, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_status(e, fn);
@@ -771,6 +772,7 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
     bool aligned = (addr(full) & 15) == 0 && plan->align % 8 == 0;
     for (int r = 0; r < owners; ++r) aligned = aligned && (addr(shards[r]) & 15) == 0;
     if (device_table) {
+        if (int rc = refuse_capture(s, fn)) return rc;
         dtab = static_cast<const uint16_t* const*>(workspace);
         const hipError_t e = hipMemcpyAsync(workspace, shards, sizeof(void*) * owners, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_status(e, fn);

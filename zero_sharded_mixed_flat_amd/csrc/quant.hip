@@ -479,6 +479,7 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards, c
     const uint8_t* const* dct = nullptr;
     const float* const* dst = nullptr;
     if (device_table) {
+        if (int rc = refuse_capture(s, fn)) return rc;
         char* w = static_cast<char*>(workspace);
         dct = reinterpret_cast<const uint8_t* const*>(w);
         dst = reinterpret_cast<const float* const*>(w + kTableBytes);
