@@ -323,6 +323,9 @@ def main():
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize FETCH_SIZE / WRITE_SIZE counter files, update profiles/traffic.json")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="touch a buffer of this many MiB before each timed step and time the steps alone with "
+                         "HIP events (the step then starts with cold caches)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step as a HIP graph after the warmup and time its replays")
     ap.add_argument("--checkpoint", metavar="DIR",
@@ -388,13 +391,29 @@ def main():
         torch.cuda.synchronize()
         step_fn = run.replay
 
-    # Whole steps, wall clock bracketed by device synchronisation.
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_fn()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / args.steps
+    if args.flush_mb > 0:
+        # Cold caches: a pass over the flush buffer before each step, which is
+        # timed alone with HIP events; ms_per_step is their median.
+        flush = torch.zeros(args.flush_mb << 20, dtype=torch.uint8, device="cuda")
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for a, b in pairs:
+            flush.add_(1)
+            a.record()
+            step_fn()
+            b.record()
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) for a, b in pairs)
+        ms_per_step = cold[len(cold) // 2]
+        del flush
+    else:
+        # Whole steps, wall clock bracketed by device synchronisation.
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step_fn()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = 1e3 * wall / args.steps
 
     # Per-kernel durations: HIP events on the stream the kernels are launched on.
     stream = torch.cuda.current_stream()
@@ -503,6 +522,7 @@ def main():
             "emulated_owners": len(run.owners), "shard_numel": run.n, "grad_dtype": w.grad_dtype,
             "param_dtype": w.param_dtype, "state_dtype": "f32", "parallelism": "one rank's share, 1 GPU",
             "hip_graph": bool(args.graph),
+            "caches": f"{args.flush_mb} MiB touched before each step" if args.flush_mb > 0 else "hot",
         },
         "hbm_gbs": step_gbs,
         "hbm_frac_of_peak": step_gbs / HBM_PEAK_GBS,
