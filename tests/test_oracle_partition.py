@@ -1,6 +1,7 @@
 """Pins for oracle.partition: the pages' worked example, brute-force coverage,
 and the shard sizes of the layouts the parity tests and the benchmark use."""
 
+import os
 import random
 
 import numpy as np
@@ -8,6 +9,16 @@ import pytest
 
 from oracle import partition
 from zero_sharded_mixed_flat_amd import workloads
+
+
+def test_printed_flat_partitions():
+    path = os.path.join(os.path.dirname(__file__), "golden", "pages_flat_partition.csv")
+    rows = [line.strip().split(",") for line in open(path) if line.strip() and not line.startswith("#")]
+    assert rows
+    for sizes, nd, per_rank, source in rows:
+        sizes = [int(x) for x in sizes.split()]
+        plan = partition.make_plan(sizes, nd=int(nd), stage=1, align=1)
+        assert [plan.real_numel(r) for r in range(int(nd))] == [int(x) for x in per_rank.split()], source
 
 
 def test_exercise6_flat_partition():
