@@ -8,6 +8,13 @@
  * to its owner; let each owner update its shard with its local optimizer
  * state; gather the updated parameters.
  *
+ * Pages cited by short name:
+ *   L18 notes         CMU 11-868 Lecture 18 notes, "Memory Optimization in Distributed Training: ZeRO" (semidirectx.com)
+ *   026 notes         "026｜ZeRO：数据并行中，没必要让每张卡保存全部训练状态" (wq-win.github.io)
+ *   L3.2              "L3.2 显存优化与 ZeRO" (yulong.wang)
+ *   Illustrated ZeRO  "图解分布式训练（八）—— ZeRO 学习" (llm.jiangnianmeng.cn)
+ *   ZeRO paper notes  "ZeRO:" paper notes (puzhiyuan.github.io)
+ *
  * Conventions for every function
  * ------------------------------
  * - Return value: ZERO_OK (0) or a negative ZERO_E* code; zero_last_error()

@@ -46,6 +46,10 @@ published formulas they restate, through library routines
 
 16-bit data is carried as ``numpy.uint16`` bit patterns with a dtype tag
 ``"f16"`` or ``"bf16"``; fp32 state is ``numpy.float32``.
+
+Pages cited by short name:
+  L3.2              "L3.2 显存优化与 ZeRO" (yulong.wang)
+  Illustrated ZeRO  "图解分布式训练（八）—— ZeRO 学习" (llm.jiangnianmeng.cn)
 """
 
 from . import accounting, partition, quant, rounding, step  # noqa: F401

@@ -13,6 +13,10 @@ Pages:
 * Elements each rank sends per step: DP, stage 1 and stage 2 move 2Ψ, stage 3
   moves 3Ψ, each times (Nd-1)/Nd for ring collectives (Lecture 18 notes §3.1;
   L3.2 §2.3; ZeRO paper notes 0x07).
+
+Pages cited by short name:
+  L3.2              "L3.2 显存优化与 ZeRO" (yulong.wang)
+  ZeRO paper notes  "ZeRO:" paper notes (puzhiyuan.github.io)
 """
 
 

@@ -23,6 +23,9 @@ Readings (the pages never mention padding or per-stage layout):
   slices before it.
 
 Everything here is exact integer arithmetic on Python ints.
+
+Pages cited by short name:
+  026 notes  "026｜ZeRO：数据并行中，没必要让每张卡保存全部训练状态" (wq-win.github.io)
 """
 
 from dataclasses import dataclass

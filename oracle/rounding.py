@@ -13,6 +13,9 @@ gradual underflow is the reading taken here.
 * bf16: written out from the definition -- bf16 is the top 16 bits of the fp32
   pattern; rounding to nearest even adds 0x7FFF plus the lowest kept bit before
   the shift.  NaN maps to the quiet NaN 0x7FC0.
+
+Pages cited by short name:
+  L3.2  "L3.2 显存优化与 ZeRO" (yulong.wang)
 """
 
 import numpy as np

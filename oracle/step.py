@@ -17,6 +17,10 @@ notes §2.2, ZeRO-1 walk-through, steps 3-5; ZeRO paper notes 0x05 §5.2):
 Everything is numpy on the CPU.  The reduce is done in float32 (the precision
 the method accumulates in); the norm is exact; Adam is evaluated in float64
 from the float32 inputs and rounded to float32 once per output.
+
+Pages cited by short name:
+  L3.2              "L3.2 显存优化与 ZeRO" (yulong.wang)
+  ZeRO paper notes  "ZeRO:" paper notes (puzhiyuan.github.io)
 """
 
 import math

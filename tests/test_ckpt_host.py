@@ -6,6 +6,9 @@ restored under another must equal the oracle's reshard bit for bit, padding
 zero; a restore followed by a step of the native host AdamW must equal the
 uninterrupted step; and every way a set of files can be incomplete or damaged
 (026 notes §五: a missing process file must fail explicitly) must raise.
+
+Pages cited by short name:
+  026 notes  "026｜ZeRO：数据并行中，没必要让每张卡保存全部训练状态" (wq-win.github.io)
 """
 
 import os

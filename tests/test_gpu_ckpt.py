@@ -4,6 +4,9 @@ Saved from HBM through pinned staging and restored into HBM under the same
 or another partition: equal to the oracle's reshard bit for bit with zero
 padding; a step after a restore equals the uninterrupted step bit for bit;
 state saved from the GPU restores into host memory (ZeRO-Offload) and back.
+
+Pages cited by short name:
+  026 notes  "026｜ZeRO：数据并行中，没必要让每张卡保存全部训练状态" (wq-win.github.io)
 """
 
 import dataclasses

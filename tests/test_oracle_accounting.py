@@ -1,6 +1,11 @@
 """Pins for oracle.accounting: every number below is printed on a source page.
 
 The fixtures in tests/golden/ name the page and section of each row.
+
+Pages cited by short name:
+  L3.2              "L3.2 显存优化与 ZeRO" (yulong.wang)
+  Illustrated ZeRO  "图解分布式训练（八）—— ZeRO 学习" (llm.jiangnianmeng.cn)
+  ZeRO paper notes  "ZeRO:" paper notes (puzhiyuan.github.io)
 """
 
 import csv

@@ -4,6 +4,9 @@
 state, keeping the parameter order and the moment belonging to each
 parameter; a single step after the restore is compared with an uninterrupted
 run, and the device count is changed.
+
+Pages cited by short name:
+  026 notes  "026｜ZeRO：数据并行中，没必要让每张卡保存全部训练状态" (wq-win.github.io)
 """
 
 import numpy as np

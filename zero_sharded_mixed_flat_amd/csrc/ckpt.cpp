@@ -14,6 +14,9 @@
 //   master | m | v   (fp32, shard_numel each, padding positions included)
 // Every array is cut into blocks of ZERO_CKPT_BLOCK elements with one
 // checksum each, so a restore verifies exactly the blocks it reads.
+//
+// Pages cited by short name:
+//   026 notes  "026｜ZeRO：数据并行中，没必要让每张卡保存全部训练状态" (wq-win.github.io)
 
 #include <fcntl.h>
 #include <hip/hip_runtime_api.h>

@@ -27,6 +27,11 @@
 //                   §2.2 step 4).
 //   gather_kernel   a4: 16-bit shards -> the unit's slice of the full buffer
 //                   (L18 notes §2.2 step 5; Illustrated ZeRO §8.4).
+//
+// Pages cited by short name:
+//   L18 notes         CMU 11-868 Lecture 18 notes, "Memory Optimization in Distributed Training: ZeRO" (semidirectx.com)
+//   L3.2              "L3.2 显存优化与 ZeRO" (yulong.wang)
+//   Illustrated ZeRO  "图解分布式训练（八）—— ZeRO 学习" (llm.jiangnianmeng.cn)
 
 #include <hip/hip_runtime.h>
 

@@ -12,6 +12,9 @@
 // paths give identical bits on every x86-64 host.  fp16 conversions use the
 // F16C instructions on the vector paths (round to nearest even) and an exact
 // software conversion on the scalar path; bf16 uses integer rounding.
+//
+// Pages cited by short name:
+//   L18 notes  CMU 11-868 Lecture 18 notes, "Memory Optimization in Distributed Training: ZeRO" (semidirectx.com)
 
 #include <hip/hip_runtime_api.h>
 #include <immintrin.h>

@@ -6,6 +6,10 @@
 // contiguous pieces, one per data-parallel rank, and a tensor may straddle two
 // ranks.  Stage 3 partitions each unit (layer) on its own so that one layer can
 // be gathered into a contiguous buffer.  All arithmetic here is int64.
+//
+// Pages cited by short name:
+//   L18 notes         CMU 11-868 Lecture 18 notes, "Memory Optimization in Distributed Training: ZeRO" (semidirectx.com)
+//   Illustrated ZeRO  "图解分布式训练（八）—— ZeRO 学习" (llm.jiangnianmeng.cn)
 
 #include <algorithm>
 #include <new>

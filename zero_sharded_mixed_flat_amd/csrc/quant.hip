@@ -15,6 +15,9 @@
 //   dequantize_kernel      codes + scales -> 16-bit
 //   gather_dequant_kernel  every owner's codes of one unit -> the unit's
 //                          16-bit slices of the full buffer
+//
+// Pages cited by short name:
+//   L18 notes  CMU 11-868 Lecture 18 notes, "Memory Optimization in Distributed Training: ZeRO" (semidirectx.com)
 
 #include <cstring>
 #include <string>

@@ -26,6 +26,9 @@ Shapes follow the pages' examples:
   elements, and every unit is gathered from all ranks' codes, dequantised
   into the 16-bit full buffer.  Slices are aligned to 256 so a block never
   straddles two owners.
+
+Pages cited by short name:
+  ZeRO paper notes  "ZeRO:" paper notes (puzhiyuan.github.io)
 """
 
 from dataclasses import dataclass, field
