@@ -5,7 +5,9 @@ The state and the 16-bit parameters are compared with the oracle's fp64
 AdamW to the same tolerance as the GPU kernel; the 16-bit conversions are
 pinned exactly (every fp16 pattern widened, fp32 values across the whole
 fp16/bf16 range narrowed against numpy's round-to-nearest-even), and every
-instruction set the CPU offers must give the same bits as the scalar path.
+instruction set the CPU offers must give the same bits as the scalar path and
+as the documented fp32 operation sequence (`fp32_sequence`), edge values
+included.
 """
 
 import numpy as np
@@ -16,6 +18,7 @@ from oracle import rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import abi
 
+import fp32_sequence
 from tolerance import AdamTrack, adam_ok
 
 HPARAMS = {
@@ -86,6 +89,32 @@ def test_five_steps_each_side_on_its_own_state(gdt, pdt):
         track.check(got, ref, (p, m, v), g, gdt, hp, t, coef, pdt, f"t={t}")
         host = got[:3]
         p, m, v = ref[:3]
+
+
+@pytest.mark.parametrize("gdt, pdt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16"), ("bf16", "f16")])
+@pytest.mark.parametrize("hp_name", sorted(HPARAMS))
+def test_evaluates_the_documented_fp32_sequence(gdt, pdt, hp_name):
+    # Bit for bit, on every instruction set: no fused multiply-add, correctly
+    # rounded division and square root, the scalars derived as documented.
+    hp = HPARAMS[hp_name]
+    g, p, m, v = fp32_sequence.edge_inputs(50_003, gdt, hp.inv_loss_scale, 21)
+    for t, coef in ((1, 1.0), (5, 0.37)):
+        ref = fp32_sequence.adamw(p, m, v, g, gdt, hp, t, coef, pdt)
+        for isa in ISAS:
+            abi.zero_cpu_set_isa(isa)
+            got = _run(g, p, m, v, gdt, pdt, hp, t, coef, threads=3)
+            for a, b, what in zip(got, ref, ("master", "m", "v", "param")):
+                fp32_sequence.same_bits(a, b, f"isa {isa} t={t} {what}")
+
+
+def test_consts_fill_follows_the_documented_derivation():
+    # The device kernel's scalars (zero_adam_consts_fill is host code).
+    for hp in HPARAMS.values():
+        for t in (1, 2, 10, 1000, 10 ** 6):
+            got = abi.zero_adam_consts_fill(_abi_hp(hp, t))
+            ref = fp32_sequence.consts(hp, t, 1.0)
+            for name, _ in abi.zero_adam_consts._fields_:
+                assert np.float32(getattr(got, name)).view(np.uint32) == ref[name].view(np.uint32), (name, t)
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

@@ -316,6 +316,9 @@ struct AdamConsts {
 // elements [b*kAdamTileElems, ...) without `vec`).
 // DEV: the scalars come from device memory (c_dev) instead of the kernel
 // arguments, so a captured graph can replay the launch with new ones.
+// The update is evaluated one fp32 operation at a time, in the order written,
+// with no fused multiply-adds; division and square root round correctly.  The
+// host AdamW evaluates the same sequence, so both give the same bits.
 template <int GDT, int PDT, bool DEV>
 __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ master,
                                                       float* __restrict__ m,
@@ -325,6 +328,7 @@ __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ ma
                                                       const float* __restrict__ coef_dev,
                                                       const int32_t* __restrict__ flag,
                                                       uint16_t* __restrict__ param) {
+#pragma clang fp contract(off)
     if (*flag != 0) return;  // a skipped step writes nothing
     const AdamConsts c = DEV ? *c_dev : c_arg;
     const float gs = c.inv_s * *coef_dev;
