@@ -17,7 +17,7 @@ import torch
 from oracle import partition, quant, rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth, workloads
-from tolerance import AdamTrack, param16_ok
+from tolerance import AdamTrack, coef_ok, norm_ok, param16_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_tiny_all_ranks_three_steps(runner):
         assert int(run.flag.item()) == 0 and not ref["skipped"]
         for i in range(w.nd):
             assert np.array_equal(synth.bits(run.reduced[i]), ref["reduced"][i]), f"reduced, owner {i}"
-        assert run.norm.item() == pytest.approx(ref["norm"], rel=1e-5)
+        norm_ok(run.norm.item(), ref["norm"], w.nd * run.n)
         assert ref["norm"] < w.max_norm and run.coef.item() == 1.0   # no clipping at this scale
         full = synth.bits(run.full)
         n = plan.shard_numel
@@ -137,7 +137,8 @@ def test_shrunk_layouts_two_steps(runner, name):
         assert int(run.flag.item()) == 0
         if not w.pre_reduced:
             assert np.array_equal(synth.bits(run.reduced[0]), reduced)
-        assert run.norm.item() == pytest.approx(norm, rel=1e-5)
+        norm_ok(run.norm.item(), norm, run.n)
+        coef_ok(run.coef.item(), coef)
         assert float(coef) < 1.0                        # clipping is active
         got = (_np32(run.master[0]), _np32(run.m[0]), _np32(run.v[0]), synth.bits(run.param_out(0)))
         bound_p = track.check(got, (p, m, v, bits), state, reduced, w.grad_dtype, hp, t, coef, w.param_dtype,

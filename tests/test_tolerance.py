@@ -2,14 +2,19 @@
 nothing grossly more: a 16-bit parameter two ulps off fails at ordinary
 magnitudes; the bounds scale with the operands of each update (so a small
 result after cancellation gets an operand-sized bound), and a planted error
-of a few hundred fp32 ulps in an ordinary element fails."""
+of a few hundred fp32 ulps in an ordinary element fails.  The norm bound
+holds against exact rational sums, even for chains built so that every
+addition loses nearly a whole rounding, and a norm accumulated in fp32 fails
+it."""
+
+from fractions import Fraction
 
 import numpy as np
 import pytest
 
 from oracle import rounding, step
 from oracle.step import AdamHparams
-from tolerance import U32, adam_bounds, adam_ok, param16_ok
+from tolerance import U32, U64, adam_bounds, adam_ok, coef_ok, norm_chain, norm_ok, norm_rel, param16_ok
 
 HP = AdamHparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
@@ -71,3 +76,65 @@ def test_planted_error_fails():
         bad[which][k] = np.float32(bad[which][k] * (1 + 300 * U32))
         with pytest.raises(AssertionError):
             adam_ok(tuple(bad), ref, (p, m, v), g, "bf16", HP, 2, coef, "bf16", f"planted in output {which}")
+
+
+def _serial(x):
+    acc = float(x[0])
+    for t in x[1:]:
+        acc += float(t)
+    return acc
+
+
+@pytest.mark.parametrize("k", [1, 7, 33, 87, 300])
+def test_summation_bound_for_nonnegative_terms(k):
+    # |S' - S| <= g(k) S for k fp64 additions of nonnegative terms.  The
+    # adversarial chain adds k terms just under half an ulp of 1 to 1: every
+    # addition rounds the term away, so the error is close to the bound and a
+    # bound smaller by a constant factor fails.
+    g = Fraction(k * U64) / (1 - Fraction(k * U64))
+    rng = np.random.default_rng(k)
+    for _ in range(20):
+        x = rng.random(k + 1) * np.exp2(rng.integers(-60, 60, k + 1).astype(np.float64))
+        exact = sum(Fraction(float(t)) for t in x)
+        assert abs(Fraction(_serial(x)) - exact) <= g * exact
+    x = np.array([1.0] + [U64 * (1 - 2.0 ** -20)] * k)
+    exact = sum(Fraction(float(t)) for t in x)
+    err = abs(Fraction(_serial(x)) - exact)
+    assert err <= g * exact
+    assert err > g * exact / 2
+
+
+def test_norm_chain_lengths():
+    assert norm_chain(1) == 33 + 10 + 27                   # one stage
+    assert norm_chain(1, n_extra=2) == 72
+    assert norm_chain(20_000_003) == 33 + 10 + (2 + 1 + 13) + 27
+    big = 10_937_500_000                                    # the 175e9 / 16-rank owner update
+    assert norm_chain(big) == 33 + 10 + (3 + 1 + 13) + 27
+    assert 40 * U64 < norm_rel(big) < 1e-14
+
+
+def test_norm_ok_separates_fp64_from_fp32_accumulation():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(1_000_000) * 1e-3).astype(np.float32).astype(np.float64)
+    sq = x * x
+    exact = sum(Fraction(float(t)) for t in sq)
+    ref = float(np.sqrt(float(exact)))
+    # numpy's pairwise fp64 sum is a tree about 30 additions deep, shallower
+    # than the kernels' (a serial sum over 1e6 terms is not, and may fail).
+    norm_ok(np.sqrt(np.sum(sq)), ref, x.size, what="fp64 pairwise")
+    acc = np.float32(0)
+    for t in sq.astype(np.float32)[:200_000]:
+        acc = np.float32(acc + t)
+    exact32 = sum(Fraction(float(t)) for t in sq[:200_000])
+    with pytest.raises(AssertionError):
+        norm_ok(np.sqrt(float(acc)), float(np.sqrt(float(exact32))), 200_000, what="fp32 accumulator")
+
+
+def test_coef_within_one_fp32_ulp():
+    ref = np.float32(0.37)
+    up = np.nextafter(ref, np.float32(1))
+    coef_ok(up, ref)
+    coef_ok(np.nextafter(ref, np.float32(0)), ref)
+    with pytest.raises(AssertionError):
+        coef_ok(np.nextafter(up, np.float32(1)), ref)
+    coef_ok(np.float32(1.0), np.float32(1.0))

@@ -21,6 +21,30 @@ update (m and v scale by b1 and b2; p by 1 + lr*wd plus lr times the change of
 m^/(sqrt(v^)+eps)) and adds each step's fresh bound.  The 16-bit parameter is
 the round-to-nearest-even of the fp32 master: within one 16-bit ulp of the
 oracle's, or within the master's bound plus one 16-bit rounding.
+
+The global norm.  The oracle's is exact up to two roundings (the exact
+rational sum of squares rounded to fp64, then a correctly rounded square
+root): relative error <= 1.5 u64, u64 = 2^-53.  The kernels form each square
+in fp64 (one rounding; the 16-bit value times a power of two is exact) and
+add the squares along a fixed tree.  Every partial sum is a sum of
+nonnegative terms, so the computed sum S' satisfies |S' - S| <= g(D+1) S with
+g(k) = k u64 / (1 - k u64) and D the largest number of additions on any
+path from a square to the root (the standard bound for recursive summation
+of nonnegative terms, Higham, "Accuracy and Stability of Numerical
+Algorithms", ch. 4).  The paths:
+  per lane           <= 33  (32 squares of a sum-of-squares range + 1 tail
+                             element; 8 in the reduce)
+  wave butterfly        6
+  block's waves      <= 4
+  fold, count > 8192  ceil(chunk / 2048) + 1, then 3 + 6 + 4
+                      (chunk <= max(4096, ceil(count / 1024)))
+  finalize            2 + 3 + 6 + 16, plus one per extra sum of squares
+where count, the number of 2048-element partial sums, is at most
+ceil(n / 2048) + 1024 (one short range per reduce call, at most 1024 calls).
+The square root halves the relative error and adds one rounding, so the
+norms differ by at most ((D + 1) / 2 + 2.5) u64 relative: about 5e-15 at
+1.1e10 elements.  The clip coefficient is one fp32 rounding of nearly equal
+fp64 quotients, so it is within one fp32 ulp of the oracle's.
 """
 
 import numpy as np
@@ -28,6 +52,7 @@ import numpy as np
 from oracle import rounding
 
 U32 = 2.0 ** -24
+U64 = 2.0 ** -53
 K_M, K_V, K_P = 4, 8, 24
 ULP16_REL = {"f16": 2.0 ** -10, "bf16": 2.0 ** -7}
 F16_MIN_ULP = 2.0 ** -24                 # fp16 subnormal spacing
@@ -111,3 +136,32 @@ def param16_ok(got_bits, ref_bits, dtype, what, master_bound=0.0):
     assert bad.size == 0, f"{what}: {bad.size} params beyond one ulp and the master's bound, " \
                           f"e.g. got {rounding.widen(np.asarray(got_bits)[bad[:3]], dtype)} " \
                           f"oracle {rounding.widen(np.asarray(ref_bits)[bad[:3]], dtype)}"
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+def norm_chain(n, n_extra=0):
+    """D: the most fp64 additions between one square and the kernels' norm."""
+    count = _ceil_div(int(n), 2048) + 1024
+    chunk = max(4096, _ceil_div(count, 1024))
+    fold = _ceil_div(chunk, 2048) + 1 + 3 + 6 + 4 if count > 8192 else 0
+    return 33 + 6 + 4 + fold + 2 + 3 + 6 + 16 + int(n_extra)
+
+
+def norm_rel(n, n_extra=0):
+    """Relative bound on |kernel norm - oracle norm| for an n-element gradient."""
+    d = norm_chain(n, n_extra)
+    return ((d + 1) / 2 + 2.5) * U64 / (1 - (d + 1) * U64)
+
+
+def norm_ok(got, ref, n, n_extra=0, what="norm"):
+    got, ref = float(got), float(ref)
+    bound = norm_rel(n, n_extra) * ref
+    assert abs(got - ref) <= bound, f"{what}: {got!r} vs oracle {ref!r}, |diff| {abs(got - ref):.3g} > {bound:.3g}"
+
+
+def coef_ok(got, ref, what="clip coefficient"):
+    got, ref = np.float32(got), np.float32(ref)
+    assert abs(float(got) - float(ref)) <= float(np.spacing(ref)), f"{what}: {got!r} vs oracle {ref!r}"
