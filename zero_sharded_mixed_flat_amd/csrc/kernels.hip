@@ -421,15 +421,30 @@ constexpr int kGatherOctsPerLane = 2;                                     // 16-
 constexpr int64_t kGatherTileOcts = int64_t(kGatherBlock) * kGatherOctsPerLane;
 constexpr int64_t kGatherTileElems = 8 * kGatherTileOcts;
 
-// Block (x, r) copies tile x of owner r's slice of one unit.  `vec` selects
-// 16-byte pieces (everything 16-byte aligned, slice a multiple of 8) or
-// element-by-element copies.
+// The hardware hands consecutive blocks of a launch to the eight XCDs in turn
+// (block b to XCD b mod 8).  xcd_grouped(b, G) renumbers the G blocks so that
+// the blocks one XCD receives take one contiguous run of tiles, the first
+// G mod 8 XCDs one tile more than the rest; it is a bijection on [0, G).  For
+// this two-stream copy that order measured 4.5% faster than launch order; the
+// other kernels, with more streams or narrower reads, were slower with it and
+// keep launch order.
+__device__ __forceinline__ int64_t xcd_grouped(int64_t b, int64_t G) {
+    const int64_t xcd = b & 7, local = b >> 3, per = G >> 3, extra = G & 7;
+    return xcd < extra ? xcd * (per + 1) + local : extra * (per + 1) + (xcd - extra) * per + local;
+}
+
+// Logical block (x, r), after xcd_grouped over the whole grid, copies tile x of
+// owner r's slice of one unit.  `vec` selects 16-byte pieces (everything
+// 16-byte aligned, slice a multiple of 8) or element-by-element copies.
 template <bool DEVICE_TABLE>
 __global__ __launch_bounds__(kGatherBlock) void gather_kernel(Ptrs64 tab, const uint16_t* const* dtab,
                                                         int64_t slice, int64_t shard_base,
                                                         int64_t full_base, int vec,
                                                         uint16_t* __restrict__ full) {
-    const int r = blockIdx.y;
+    const int64_t gx = gridDim.x;
+    const int64_t b = xcd_grouped(int64_t(blockIdx.y) * gx + blockIdx.x, gx * gridDim.y);
+    const int64_t bx = b % gx;
+    const int r = static_cast<int>(b / gx);
     const uint16_t* src;
     if constexpr (DEVICE_TABLE) src = dtab[r];
     else src = tab.p[r];
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(kGatherBlock) void gather_kernel(Ptrs64 tab, const 
         const u4* s4 = reinterpret_cast<const u4*>(src);
         u4* d4 = reinterpret_cast<u4*>(dst);
         const int64_t nv = slice / 8;
-        const int64_t t0 = int64_t(blockIdx.x) * kGatherTileOcts + threadIdx.x;
+        const int64_t t0 = bx * kGatherTileOcts + threadIdx.x;
         if (t0 - threadIdx.x + kGatherTileOcts <= nv) {
             u4 x[kGatherOctsPerLane];
 #pragma unroll
@@ -453,7 +468,7 @@ __global__ __launch_bounds__(kGatherBlock) void gather_kernel(Ptrs64 tab, const 
             }
         }
     } else {
-        const int64_t e0 = int64_t(blockIdx.x) * kGatherTileElems;
+        const int64_t e0 = bx * kGatherTileElems;
         const int64_t e1 = e0 + kGatherTileElems < slice ? e0 + kGatherTileElems : slice;
         for (int64_t e = e0 + threadIdx.x; e < e1; e += kGatherBlock) dst[e] = src[e];
     }
