@@ -162,11 +162,14 @@ def _short(name):
     return name.replace("void ", "").split("(")[0]
 
 
-def summarize_trace(stats_csv, command):
+def summarize_trace(stats_csv, command, bench_log=None):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run: its kernel
     statistics (this library's kernels first), then the same dispatches from
     the per-dispatch trace grouped by kernel and grid size, which separates
-    launches of one kernel that do different work."""
+    launches of one kernel that do different work.  With ``bench_log`` (the
+    output of the profiled bench.py run) it adds bench.py's own HIP-event
+    time per launch of the roofline kernel in that same process beside
+    rocprofv3's average for that kernel's busiest grid size."""
     import csv
     from collections import defaultdict
     rows = list(csv.DictReader(open(stats_csv)))
@@ -189,7 +192,34 @@ def summarize_trace(stats_csv, command):
                 "| kernel | grid (threads) | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
         for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             out.append(f"| `{name}` | {grid} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+        if bench_log:
+            out += _bench_agreement(bench_log, groups)
     return "\n".join(out) + "\n"
+
+
+def _bench_agreement(bench_log, groups):
+    """bench.py's JSON line from the profiled run against the trace of the same run."""
+    lines = [ln for ln in open(bench_log) if ln.startswith('{"metric"')]
+    if not lines:
+        raise RuntimeError(f"{bench_log} holds no bench.py result line")
+    d = json.loads(lines[-1])
+    rf = d["roofline"]
+    out = ["", "bench.py's result line from the profiled run (the same process):", "",
+           f"* `value` {d['value']:.4g} {d['unit']}, {d['ms_per_step']:.3f} ms per step "
+           f"({d['steps']} steps after {d['warmup']} warmup)."]
+    cands = [(k, v) for k, v in groups.items() if k[0].split("<")[0] == rf["kernel"]]
+    if not cands:
+        out.append(f"* roofline kernel `{rf['kernel']}` runs no GPU dispatch to compare.")
+        return out
+    (name, grid), durs = max(cands, key=lambda kv: sum(kv[1]))
+    trace_us = sum(durs) / len(durs)
+    hip_us = rf["launch_ms"] * 1e3
+    out.append(f"* roofline kernel `{rf['kernel']}`: {hip_us:.1f} us per launch by HIP events on its stream "
+               f"({rf['launches_per_step']} launch(es) per step; the events bracket the phase, so gaps between "
+               f"launches count) against {trace_us:.1f} us average for `{name}` at grid {grid} in this trace: "
+               f"ratio {hip_us / trace_us:.3f}. Achieved {rf['achieved']:.0f} {rf['unit']} of {rf['peak']:.0f} "
+               f"(frac {rf['frac']:.3f}).")
+    return out
 
 
 def summarize_counters(fetch_csv, write_csv, phases, commands):
@@ -321,6 +351,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-trace", metavar="STATS_CSV",
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--bench-line", metavar="LOG", default=None,
+                    help="with --summarize-trace: the profiled bench.py run's output, to compare its timing")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize FETCH_SIZE / WRITE_SIZE counter files, update profiles/traffic.json")
     ap.add_argument("--flush-mb", type=int, default=0,
@@ -336,7 +368,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, "\n".join(args.command)), end="")
+        print(summarize_trace(args.summarize_trace, "\n".join(args.command), args.bench_line), end="")
         return 0
     if args.summarize_counters:
         from zero_sharded_mixed_flat_amd import abi as _abi
