@@ -250,14 +250,18 @@ typedef struct {
 /*
  * zero_adam_step -- the owner updates its fp32 variance, momentum and master,
  * then copies the master to the 16-bit parameter (L18 notes §2.2 step 4;
- * Adam is elementwise, §2.1).  Per element, in fp32:
- *   g  = f32(grad[i]) * inv_loss_scale * (*coef_dev)
- *   m  = beta1 m + (1 - beta1) g
- *   v  = beta2 v + (1 - beta2) g^2
- *   p  = p - lr * ( (m / bc1) / (sqrt(v / bc2) + eps) + weight_decay * p )
+ * Adam is elementwise, §2.1).  Per element, one IEEE fp32 rounding per
+ * operation in this order, no fused multiply-add, correctly rounded division
+ * and square root:
+ *   g  = f32(grad[i]) * (inv_loss_scale * (*coef_dev))
+ *   m  = beta1*m + (1 - beta1)*g
+ *   v  = beta2*v + (1 - beta2)*(g*g)
+ *   p  = p - lr * ((m * inv_bc1) / (sqrt(v * inv_bc2) + eps) + weight_decay*p)
  *   param_out[i] = round_to_nearest_even_16(p)
- * master, m and v are each read once and written once.  If *flag != 0 the
- * kernel writes nothing (the step is skipped).
+ * with the scalars of zero_adam_consts_fill.  zero_cpu_adam_step evaluates
+ * the same sequence, so the two give identical bits.  master, m and v are
+ * each read once and written once.  If *flag != 0 the kernel writes nothing
+ * (the step is skipped).
  *
  * master, m, v: device fp32, n each, distinct.  grad: device 16-bit
  * (`grad_dtype`), n.  coef_dev: device fp32 (from zero_grad_norm).  flag:
@@ -269,8 +273,8 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
                    const int32_t* flag, void* param_out, int param_dtype, void* stream);
 
 /* The fp32 scalars of one AdamW step, as zero_adam_step derives them from
- * zero_adam_hparams: 1 - beta formed in fp32, bias corrections f32(1 - beta^t)
- * from fp64 and their fp32 reciprocals. */
+ * zero_adam_hparams: 1 - beta, the bias corrections bc = 1 - beta^t and their
+ * reciprocals inv_bc = 1 / bc, each formed in fp64 and rounded to fp32. */
 typedef struct {
     float lr, beta1, beta2, one_minus_beta1, one_minus_beta2, eps, weight_decay, inv_loss_scale;
     float inv_bias_corr1, inv_bias_corr2;
@@ -456,9 +460,9 @@ int zero_ckpt_load(const char* const* paths, int n_paths, const zero_plan* plan,
  * zero_cpu_adam_step -- the AdamW update of zero_adam_step on HOST memory, for
  * ZeRO-Offload, which keeps the fp32 master, m and v (12 bytes per parameter)
  * in host memory and updates them with a multi-threaded, vectorised CPU Adam
- * (L18 notes §4.4).  Same formula and the same fp32 operation sequence as the
- * GPU kernel (no fused multiply-add), with g = f32(grad) * inv_loss_scale *
- * coef; the result does not depend on n_threads or on the instruction set.
+ * (L18 notes §4.4).  The fp32 operation sequence of zero_adam_step, with
+ * coef in place of *coef_dev, so it gives the GPU kernel's bits; the result
+ * does not depend on n_threads or on the instruction set.
  *
  * master, m, v: host fp32, n each, distinct, 4-byte aligned.  grad: host
  * 16-bit (`grad_dtype`), n.  param_out: host 16-bit (`param_dtype`), n.  coef:
