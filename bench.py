@@ -448,13 +448,23 @@ def main():
         ms_per_step = 1e3 * wall / args.steps
 
     # Per-kernel durations: HIP events on the stream the kernels are launched on.
+    # Every step is enqueued before any is waited for, behind a few ms of
+    # queued work, so the host runs ahead of the GPU and an event pair times
+    # its kernels, not the host preparing the launch.  Where the host is the
+    # slower side (a launch-bound workload) the gaps remain in the figures.
     stream = torch.cuda.current_stream()
     phases = ["reduce", "norm", "adam", "quantize", "gather"]
     acc = {p: 0.0 for p in phases}
     step_ms = []
+    lead = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(10):
+        lead.add_(1)
+    events = []
     for _ in range(args.steps):
         ev = {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for p in phases + ["step"]}
+        events.append(ev)
         ev["step"][0].record(stream)
         run.flag.zero_()
         if not w.pre_reduced:
@@ -477,7 +487,9 @@ def main():
             ev["gather"][1].record(stream)
         ev["step"][1].record(stream)
         run.t += 1
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    del lead
+    for ev in events:
         step_ms.append(ev["step"][0].elapsed_time(ev["step"][1]))
         for p in phases:
             if (p == "reduce" and w.pre_reduced or p == "gather" and run.shards is None
