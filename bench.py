@@ -151,6 +151,36 @@ def cpu_baseline(run, budget_s=12.0):
     }, parity
 
 
+def host_copy_gbs(threads, nbytes=1 << 31):
+    """Host memory copy bandwidth (read + write bytes per second / 1e9) with ``threads`` threads."""
+    import torch
+    saved = torch.get_num_threads()
+    torch.set_num_threads(threads)
+    try:
+        a = torch.ones(nbytes // 4, dtype=torch.float32)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        best = float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            b.copy_(a)
+            best = min(best, time.perf_counter() - t0)
+        return 2 * nbytes / best / 1e9
+    finally:
+        torch.set_num_threads(saved)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _gather_label(w):
     if w.gather_bits != 16:
         return f", INT{w.gather_bits} quantise + {w.nd} dequantising gathers"
@@ -600,6 +630,8 @@ def main():
     if not args.no_cpu_baseline:
         _log("bench: timing the CPU oracle on a sample")
         cb, parity = cpu_baseline(run)
+        cb["gbs"] = cb["value"] * alg_bytes / owned / 1e9   # the step's algorithmic bytes per parameter
+        cb["cpu"] = cpu_model()
         result["cpu_baseline"] = cb
         result["sample_parity_reduced_bit_exact"] = parity
     print(json.dumps(result), flush=True)
