@@ -422,8 +422,8 @@ def main():
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU exchange is design-only)", file=sys.stderr)
+        print(f"bench.py measures one GPU's share of the step; --gpus {args.gpus} is not supported: "
+              "the exchange between GPUs is not implemented", file=sys.stderr)
         return 2
 
     import torch
