@@ -197,6 +197,25 @@ def test_gather_rejects():
     abi.zero_gather_params(**dict(base, unit_begin=1, unit_end=1))   # empty range: no-op
 
 
+def test_gather_rejects_above_64_owners():
+    # The pointer table goes into the workspace: it must exist and overlap
+    # neither the full buffer nor any shard.
+    plan = abi.Plan([1000], 100, 3, 8)
+    shard_bytes = 2 * plan.rank(0)[0]
+    shards = [A + i * 4096 for i in range(100)]
+    base = dict(plan=plan, shards=shards, unit_begin=0, unit_end=1, dtype=1, full=B, workspace=W, stream=0,
+                workspace_bytes=abi.zero_workspace_bytes(0, 0))
+    assert shard_bytes <= 4096
+    for bad, code in ((dict(workspace=None, workspace_bytes=0), abi.ZERO_EINVAL),
+                      (dict(workspace_bytes=100), abi.ZERO_EINVAL),
+                      (dict(workspace=B + 64), abi.ZERO_EALIAS),
+                      (dict(workspace=shards[57] + 16), abi.ZERO_EALIAS)):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_gather_params(**dict(base, **bad))
+        assert e.value.code == code, bad
+    assert "workspace overlaps shard 57" in str(e.value)
+
+
 def test_quant_sizes():
     assert abi.zero_quant_code_bytes(1000, 8) == 1000
     assert abi.zero_quant_code_bytes(1001, 4) == 501
@@ -234,6 +253,23 @@ def test_gather_dequant_rejects():
     with pytest.raises(abi.ZeroError) as e:
         abi.zero_gather_dequant(plan, [A, A + 8, A, A], [W] * 4, 0, 2, 8, 1, B, stream=0)   # codes not 16-aligned
     assert e.value.code == abi.ZERO_EINVAL and "shard 1" in str(e.value)
+
+
+def test_gather_dequant_rejects_above_64_owners():
+    # Both pointer tables go into the workspace's first 16 KiB: it must exist
+    # and overlap neither the full buffer nor any code or scale shard.
+    plan = abi.Plan([256 * 100], 100, 3, 256)
+    codes = [A + i * 4096 for i in range(100)]
+    scales = [F + i * 64 for i in range(100)]
+    base = dict(plan=plan, code_shards=codes, scale_shards=scales, unit_begin=0, unit_end=1, bits=8, dtype=1,
+                full=B, workspace=W, stream=0, workspace_bytes=abi.zero_workspace_bytes(0, 0))
+    for bad, code, text in ((dict(workspace=None, workspace_bytes=0), abi.ZERO_EINVAL, "workspace"),
+                            (dict(workspace=B + 64), abi.ZERO_EALIAS, "full buffer"),
+                            (dict(workspace=codes[70] - 1024), abi.ZERO_EALIAS, "overlaps shard 70"),
+                            (dict(workspace=scales[99]), abi.ZERO_EALIAS, "overlaps shard 99")):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_gather_dequant(**dict(base, **bad))
+        assert e.value.code == code and text in str(e.value), (bad, str(e.value))
 
 
 def test_pointer_table():

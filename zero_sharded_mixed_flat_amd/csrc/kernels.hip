@@ -788,6 +788,9 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
             return fail(ZERO_EINVAL, std::string(fn) + ": more than 64 owners need a workspace of zero_workspace_bytes(0, 0) bytes");
         if (overlaps(workspace, kTableBytes, full, full_bytes))
             return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps the full buffer");
+        for (int r = 0; r < owners; ++r)
+            if (overlaps(workspace, kTableBytes, shards[r], shard_bytes))
+                return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps shard " + std::to_string(r));
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
