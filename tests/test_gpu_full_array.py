@@ -3,7 +3,8 @@
 Every element of the rank's step is compared with the oracle: the reduced
 gradient bit for bit, the exact norm of the whole reduced gradient (the sum of
 the oracle's exact per-chunk sums of squares), and master, m, v and the
-16-bit parameters to the derived tolerance.  The inputs are the workload's
+16-bit parameters to the derived tolerance, and bit for bit to the documented
+fp32 sequence (tests/fp32_sequence.py) with the device's clip multiplier.  The inputs are the workload's
 own seeded draws (no tiling), copied to the host before the step; the oracle
 runs chunk by chunk on host threads (numpy releases the interpreter lock in
 its array operations).
@@ -19,6 +20,7 @@ import torch
 
 from oracle import step
 from oracle.step import AdamHparams
+import fp32_sequence
 from tolerance import adam_ok, coef_ok, norm_ok
 from zero_sharded_mixed_flat_amd import synth, workloads
 
@@ -84,6 +86,7 @@ def test_full_array_step(runner, name):
     assert float(coef) < 1.0                                  # clipping is active
     hp = AdamHparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                      inv_loss_scale=w.inv_loss_scale, max_norm=w.max_norm)
+    dev_coef = np.float32(run.coef.item())
 
     def adam_chunk(c):
         lo, hi = c
@@ -91,6 +94,10 @@ def test_full_array_step(runner, name):
         ref = step.adam_update(*inputs, reduced_ref[lo], w.grad_dtype, hp, 1, coef, w.param_dtype)
         got = tuple(s[lo:hi] for s in state_gpu) + (param_gpu[lo:hi],)
         adam_ok(got, ref, inputs, reduced_ref[lo], w.grad_dtype, hp, 1, coef, w.param_dtype, f"[{lo}, {hi})")
+        # bit for bit: the documented fp32 sequence with the multiplier the device computed
+        seq = fp32_sequence.adamw(*inputs, reduced_ref[lo], w.grad_dtype, hp, 1, dev_coef, w.param_dtype)
+        for a, b, what in zip(got, seq, ("master", "m", "v", "param")):
+            fp32_sequence.same_bits(a, b, f"{what} [{lo}, {hi})")
         return hi - lo
 
     with ThreadPoolExecutor(THREADS) as ex:
@@ -141,6 +148,7 @@ def test_full_shard_zero3_and_gathered_layers(runner):
     assert float(coef) < 1.0
     hp = AdamHparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                      inv_loss_scale=w.inv_loss_scale, max_norm=w.max_norm)
+    dev_coef = np.float32(run.coef.item())
     bits_ref = np.empty(n, np.uint16)
 
     def adam_chunk(c):
@@ -149,6 +157,10 @@ def test_full_shard_zero3_and_gathered_layers(runner):
         ref = step.adam_update(*inputs, reduced_ref[lo], w.grad_dtype, hp, 1, coef, w.param_dtype)
         got = tuple(s[lo:hi] for s in state_gpu) + (param_gpu[lo:hi],)
         adam_ok(got, ref, inputs, reduced_ref[lo], w.grad_dtype, hp, 1, coef, w.param_dtype, f"[{lo}, {hi})")
+        # bit for bit: the documented fp32 sequence with the multiplier the device computed
+        seq = fp32_sequence.adamw(*inputs, reduced_ref[lo], w.grad_dtype, hp, 1, dev_coef, w.param_dtype)
+        for a, b, what in zip(got, seq, ("master", "m", "v", "param")):
+            fp32_sequence.same_bits(a, b, f"{what} [{lo}, {hi})")
         bits_ref[lo:hi] = ref[3]
         return hi - lo
 
@@ -196,12 +208,16 @@ def test_sampled_chunks_owner_update_175b(runner):
     assert float(coef) < 1.0
     hp = AdamHparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                      inv_loss_scale=w.inv_loss_scale, max_norm=w.max_norm)
+    dev_coef = np.float32(run.coef.item())
     got_all = {o: tuple(t[0, o:o + CHUNK].cpu().numpy() for t in (run.master, run.m, run.v))
                + (_host16(run.param_out(0)[o:o + CHUNK]),) for o in offs}
 
     def check(o):
         ref = step.adam_update(*states[o], grads[o], w.grad_dtype, hp, 1, coef, w.param_dtype)
         adam_ok(got_all[o], ref, states[o], grads[o], w.grad_dtype, hp, 1, coef, w.param_dtype, f"@ {o}")
+        seq = fp32_sequence.adamw(*states[o], grads[o], w.grad_dtype, hp, 1, dev_coef, w.param_dtype)
+        for a, b, what in zip(got_all[o], seq, ("master", "m", "v", "param")):
+            fp32_sequence.same_bits(a, b, f"{what} @ {o}")
         return CHUNK
 
     with ThreadPoolExecutor(THREADS) as ex:
