@@ -4,7 +4,8 @@ The reduced gradient and the clip multiplier live on the GPU, the fp32 state
 in host memory; the host state and the 16-bit parameters that come back to
 the device are compared with the oracle's AdamW, and bit for bit with the host
 AdamW called directly on the same inputs (the chunking and the overlap of
-copies with the update change nothing).  Staging buffers down to the minimum
+copies with the update change nothing) and with the GPU kernel keeping the
+state in HBM.  Staging buffers down to the minimum
 force many chunks and a ragged last one.
 """
 
@@ -77,6 +78,17 @@ def test_offload_matches_oracle_and_host_adam(abi, gdt, pdt, n, staging):
     abi.zero_cpu_adam_step(hm, hmm, hv, torch.from_numpy(g.view(np.int16).copy()), gdt, n, _abi_hp(abi, HP, 3),
                            float(coef), False, out, pdt, 2)
     for a, b in zip(got, (hm.numpy(), hmm.numpy(), hv.numpy(), out.numpy().view(np.uint16))):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+    # and by the GPU kernel with the state kept in HBM: the offloaded step gives the same bits
+    dm, dmm, dv = (torch.from_numpy(a.copy()).cuda() for a in (p, m, v))
+    dpar = torch.zeros(n, dtype=torch.int16, device="cuda")
+    abi.zero_adam_step(dm, dmm, dv, torch.from_numpy(g.view(np.int16).copy()).cuda(), gdt, n, _abi_hp(abi, HP, 3),
+                       torch.tensor([coef], dtype=torch.float32, device="cuda"),
+                       torch.zeros(1, dtype=torch.int32, device="cuda"), dpar, pdt)
+    torch.cuda.synchronize()
+    for a, b in zip(got, (dm.cpu().numpy(), dmm.cpu().numpy(), dv.cpu().numpy(),
+                          dpar.cpu().numpy().view(np.uint16))):
         assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                               b.view(np.uint32) if b.dtype == np.float32 else b)
 
