@@ -411,9 +411,11 @@ int zero_plan_reshard(const zero_plan* old_plan, const zero_plan* new_plan, int 
  * a resumable checkpoint holds the sharded optimizer state, not only the
  * weights).  Layout: a 4 KiB-aligned header (magic, version, Nd, stage,
  * align, rank, step, the unit sizes, one 64-bit checksum per 1 MiB block of
- * each array), then the three arrays.  The file is written as `path`.tmp,
+ * each array), then the three arrays.  The file is written under a
+ * temporary name unique to the process and call (`path`.tmp.<pid>.<n>),
  * flushed to stable storage and renamed (and the directory flushed), so
- * `path` never names a partial file.  `location`: ZERO_LOC_DEVICE
+ * `path` never names a partial file; of two saves to one path, the later
+ * rename wins.  `location`: ZERO_LOC_DEVICE
  * (arrays in device memory, copied out through `staging` on `stream`) or
  * ZERO_LOC_HOST.  staging: pinned host memory, >= ZERO_CKPT_MIN_STAGING
  * bytes, 64-byte aligned.  Blocks until the file is complete.  Errors:

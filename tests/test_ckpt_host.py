@@ -201,6 +201,37 @@ def test_missing_foreign_and_damaged_files(tmp_path):
     assert "not a checkpoint" in str(load_error([paths[0], damaged] + paths[2:]))
 
 
+def test_concurrent_saves_to_one_path(tmp_path):
+    # Each save writes its own temporary file: eight threads saving different
+    # states to one path leave exactly one whole file, equal to one of them.
+    import threading
+    plan, ref = _plans([50_000], 2, 2, 8)
+    n = ref.shard_numel
+    path = str(tmp_path / "r0.zck")
+    states = [[torch.full((n,), float(k + a)) for a in range(3)] for k in range(8)]
+    errors = []
+
+    def save(k):
+        try:
+            abi.zero_ckpt_save(path, plan, 0, 5, *states[k], _staging())
+        except Exception as exc:                                   # noqa: BLE001
+            errors.append(exc)
+
+    threads = [threading.Thread(target=save, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors
+    assert os.listdir(tmp_path) == ["r0.zck"]                      # no temporary file left behind
+    abi.zero_ckpt_save(str(tmp_path / "r1.zck"), plan, 1, 5, *states[0], _staging())
+    out = [torch.empty(n) for _ in range(3)]
+    assert abi.zero_ckpt_load([path, str(tmp_path / "r1.zck")], plan, 0, *out, _staging()) == 5
+    # rank 0's file is exactly one of the eight saves, whole (a torn mix of
+    # two would also fail the block checksums)
+    assert sum(all(torch.equal(o, st) for o, st in zip(out, states[k])) for k in range(8)) == 1
+
+
 def test_save_rejects_and_leaves_nothing(tmp_path):
     plan, ref = _plans([1000], 2, 2, 8)
     t = [torch.zeros(ref.shard_numel) for _ in range(3)]

@@ -24,6 +24,7 @@
 #include <unistd.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cerrno>
 #include <cstdint>
 #include <cstring>
@@ -269,9 +270,13 @@ int zero_ckpt_save(const char* path, const zero_plan* plan, int rank, int64_t st
     // A stage-3 plan lists its units; stages 0-2 merge them into one, which
     // loses nothing a restore needs (the flat order is the same).
 
-    const std::string tmp = std::string(path) + ".tmp";
+    // The temporary name is unique to this process and call, so two saves to
+    // one path never write the same file; the last rename wins, whole.
+    static std::atomic<uint64_t> save_serial{0};
+    const std::string tmp = std::string(path) + ".tmp." + std::to_string(::getpid()) + "." +
+                            std::to_string(save_serial.fetch_add(1));
     Fd out;
-    out.fd = ::open(tmp.c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
+    out.fd = ::open(tmp.c_str(), O_WRONLY | O_CREAT | O_EXCL | O_CLOEXEC, 0644);
     if (out.fd < 0) return fail(ZERO_EIO, std::string(fn) + ": cannot create '" + tmp + "': " + sys_reason());
     auto abandon = [&](int rc) {
         ::close(out.fd);
