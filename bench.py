@@ -14,6 +14,12 @@ events on the stream the kernels run on.  ``cpu_baseline`` is
 the CPU oracle timed on a bounded sample of the same workload's inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--graph] [--flush-mb MB] [--no-cpu-baseline]
+  --workload NAME   any workload of zero_sharded_mixed_flat_amd/workloads.py
+  --graph           time replays of the step captured once as a HIP graph
+  --flush-mb MB     touch MB MiB before each step (cold caches); time the steps alone
+  --checkpoint DIR  instead: save and restore throughput of sharded optimizer state
+  --summarize-trace / --summarize-counters  turn rocprofv3 output into profiles/ summaries
 """
 
 import argparse
