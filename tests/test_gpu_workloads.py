@@ -9,7 +9,8 @@ gradient is tiled too and its exact sum of squares is
 (reduced gradient bit for bit, master/m/v, 16-bit parameters, gathered
 buffer) is compared on sampled chunks of 2^20 elements -- first, last, 16
 random ones and unit boundaries -- computed one by one by the oracle from the
-actual device inputs copied back before the step.
+actual device inputs copied back before the step; master/m/v and the 16-bit
+parameters also bit for bit against the documented fp32 sequence.
 """
 
 import gc
@@ -21,6 +22,7 @@ import torch
 from oracle import partition, quant, rounding, step
 from oracle.step import AdamHparams
 from zero_sharded_mixed_flat_amd import synth, workloads
+import fp32_sequence
 from tolerance import adam_ok, coef_ok, norm_ok
 
 pytestmark = pytest.mark.gpu
@@ -167,6 +169,7 @@ def test_full_size_step(runner, name):
     norm_ok(run.norm.item(), norm, n)
     coef_ok(run.coef.item(), coef)
     assert float(coef) < 1.0                                  # clipping is active
+    dev_coef = np.float32(run.coef.item())
 
     for o in offs:
         contribs, grad, (p0, m0, v0) = chunks[o]
@@ -180,6 +183,9 @@ def test_full_size_step(runner, name):
         got = tuple(t[0, o:o + CHUNK].cpu().numpy() for t in (run.master, run.m, run.v))
         got += (synth.bits(run.param_out(0)[o:o + CHUNK]),)
         adam_ok(got, (p, m, v, bits), (p0, m0, v0), reduced, w.grad_dtype, hp, 1, coef, w.param_dtype, f"@ {o}")
+        seq = fp32_sequence.adamw(p0, m0, v0, reduced, w.grad_dtype, hp, 1, dev_coef, w.param_dtype)
+        for a, b, what in zip(got, seq, ("master", "m", "v", "param")):
+            fp32_sequence.same_bits(a, b, f"{what} @ {o}")   # on the GPU and on the host (offload) alike
         if run.codes is not None:
             _check_quantised_gather(run, plan, w, o, others, bits)
         elif others is not None:
