@@ -112,9 +112,10 @@ typedef struct {
  * are padding.  Units are laid out back to back in the padded full buffer,
  * and their slices back to back in every rank's shard.
  *
- * unit_numels: host array of n_units sizes >= 0 (sum > 0); 1 <= nd <= 1024;
- * align_elems >= 1.  On success *out receives a plan the caller frees with
- * zero_plan_destroy.  Errors: ZERO_EINVAL, ZERO_ENOMEM.
+ * unit_numels: host array of n_units sizes >= 0 (sum > 0, at most 2^50);
+ * 1 <= nd <= 1024; 1 <= align_elems <= 2^30; the padded layout (full_numel)
+ * must stay within 2^52 elements.  On success *out receives a plan the caller
+ * frees with zero_plan_destroy.  Errors: ZERO_EINVAL, ZERO_ENOMEM.
  */
 int zero_plan_create(const int64_t* unit_numels, int n_units, int nd, int stage,
                      int64_t align_elems, zero_plan** out);

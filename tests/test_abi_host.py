@@ -87,6 +87,13 @@ def test_plan_rejects_bad_arguments():
         with pytest.raises(abi.ZeroError) as e:
             abi.Plan(*args)
         assert e.value.code == abi.ZERO_EINVAL
+    # the padded layout is bounded: 4096 one-element layers padded to 2^30 on
+    # 1024 owners fill exactly 2^52 elements; one layer more is rejected
+    assert abi.Plan([1] * 4096, 1024, 3, 1 << 30).full_numel() == 1 << 52
+    with pytest.raises(abi.ZeroError) as e:
+        abi.Plan([1] * 4097, 1024, 3, 1 << 30)
+    assert e.value.code == abi.ZERO_EINVAL and "2^52" in str(e.value)
+    assert abi.Plan([1 << 50], 1024, 1, 1 << 30).full_numel() == 1 << 50      # the largest real size
     p = abi.Plan([10, 20], 2, 3, 8)
     with pytest.raises(abi.ZeroError):
         p.segments([10, 21], 0)          # sizes do not add up

@@ -131,6 +131,12 @@ int zero_plan_create(const int64_t* unit_numels, int n_units, int nd, int stage,
         for (int64_t u : sizes) {
             int64_t per = (u + p->owners - 1) / p->owners;
             int64_t s = (per + align_elems - 1) / align_elems * align_elems;
+            // padding can outgrow the 2^50 real elements (up to align per unit
+            // and owner): keep the padded layout within 2^52 elements
+            if (s > (int64_t(1) << 52) / p->owners || full_base > (int64_t(1) << 52) - int64_t(p->owners) * s) {
+                delete p;
+                return zf::fail(ZERO_EINVAL, "zero_plan_create: the padded layout exceeds 2^52 elements");
+            }
             p->units.push_back({u, s, full_base, shard_base});
             full_base += int64_t(p->owners) * s;
             shard_base += s;
