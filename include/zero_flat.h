@@ -67,6 +67,11 @@ extern "C" {
 
 #define ZERO_MAX_RANKS 1024
 
+/* The most elements one call processes (n, or a unit's slice): 2^41, more than
+ * any device holds.  Larger sizes are rejected with ZERO_EINVAL, so no launch
+ * grid can exceed its hardware limit. */
+#define ZERO_MAX_ELEMS (INT64_C(1) << 41)
+
 /* Bits of the int32 step flag (device memory, OR-ed by the kernels). */
 #define ZERO_FLAG_NONFINITE_GRAD 1 /* an input or reduced gradient is inf/NaN */
 #define ZERO_FLAG_NONFINITE_NORM 2 /* the sum of squares is not finite */

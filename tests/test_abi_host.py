@@ -223,6 +223,31 @@ def test_gather_rejects_above_64_owners():
     assert "workspace overlaps shard 57" in str(e.value)
 
 
+def test_sizes_beyond_the_element_limit_are_rejected():
+    # No launch grid may exceed its hardware limit: every call refuses more
+    # than ZERO_MAX_ELEMS elements before anything is enqueued.
+    big = abi.ZERO_MAX_ELEMS + 1
+    assert abi.zero_workspace_bytes(abi.ZERO_MAX_ELEMS, 1024) > 0
+    with pytest.raises(abi.ZeroError):
+        abi.zero_workspace_bytes(big, 1)
+    ws = 1 << 45
+    calls = [
+        lambda: abi.zero_reduce_shard([A, A + 4096], big, abi.ZERO_F16, 1.0, B, W, 0, F, stream=0,
+                                      workspace_bytes=ws),
+        lambda: abi.zero_grad_norm(B, big, 1, 1.0, W, 1, None, 0, 1.0, F, F + 8, F + 16, stream=0,
+                                   workspace_bytes=ws),
+        lambda: _adam(n=big),
+        lambda: abi.zero_quantize_blocks(A, "f16", big, 8, B, W, stream=0),
+        lambda: abi.zero_dequantize_blocks(A, W, big, 8, B, "f16", stream=0),
+        lambda: abi.zero_gather_params(abi.Plan([big], 1, 3, 8), [A], 0, 1, 1, B, None, stream=0),
+        lambda: abi.zero_gather_dequant(abi.Plan([big + 255], 1, 3, 256), [A], [W], 0, 1, 8, 1, B, stream=0),
+    ]
+    for k, call in enumerate(calls):
+        with pytest.raises(abi.ZeroError) as e:
+            call()
+        assert e.value.code == abi.ZERO_EINVAL and "2^41" in str(e.value), k
+
+
 def test_quant_sizes():
     assert abi.zero_quant_code_bytes(1000, 8) == 1000
     assert abi.zero_quant_code_bytes(1001, 4) == 501

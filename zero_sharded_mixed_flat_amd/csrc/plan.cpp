@@ -290,7 +290,7 @@ int zero_comm_volume(double psi, int nd, int stage, double* elems_sent) {
 }
 
 int64_t zero_workspace_bytes(int64_t n, int n_sets) {
-    if (n < 0 || n_sets < 0 || n_sets > ZERO_MAX_RANKS) {
+    if (n < 0 || n > ZERO_MAX_ELEMS || n_sets < 0 || n_sets > ZERO_MAX_RANKS) {
         zf::fail(ZERO_EINVAL, "zero_workspace_bytes: bad argument");
         return -1;
     }
