@@ -67,10 +67,12 @@ extern "C" {
 
 #define ZERO_MAX_RANKS 1024
 
-/* The most elements one call processes (n, or a unit's slice): 2^41, more than
- * any device holds.  Larger sizes are rejected with ZERO_EINVAL, so no launch
- * grid can exceed its hardware limit. */
-#define ZERO_MAX_ELEMS (INT64_C(1) << 41)
+/* The most elements one call processes (n, or a unit's slice): 2^34.  A
+ * launch's size per dimension is a 32-bit count of work-items, and at 2^34
+ * elements the largest grid here (the reduce, 256 threads per 2048 elements)
+ * is 2^31 work-items.  Larger sizes are rejected with ZERO_EINVAL; callers
+ * split them into several calls. */
+#define ZERO_MAX_ELEMS (INT64_C(1) << 34)
 
 /* Bits of the int32 step flag (device memory, OR-ed by the kernels). */
 #define ZERO_FLAG_NONFINITE_GRAD 1 /* an input or reduced gradient is inf/NaN */

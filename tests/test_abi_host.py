@@ -223,6 +223,14 @@ def test_gather_rejects_above_64_owners():
     assert "workspace overlaps shard 57" in str(e.value)
 
 
+def test_every_workload_fits_the_element_limit():
+    for name, w in workloads.WORKLOADS.items():
+        plan = abi.Plan(w.units, w.nd, w.stage, w.align)
+        n, _ = plan.rank(0)
+        assert n <= abi.ZERO_MAX_ELEMS, name
+        assert all(plan.unit(u)[1] <= abi.ZERO_MAX_ELEMS for u in range(plan.info()["n_units"])), name
+
+
 def test_sizes_beyond_the_element_limit_are_rejected():
     # No launch grid may exceed its hardware limit: every call refuses more
     # than ZERO_MAX_ELEMS elements before anything is enqueued.
@@ -245,7 +253,7 @@ def test_sizes_beyond_the_element_limit_are_rejected():
     for k, call in enumerate(calls):
         with pytest.raises(abi.ZeroError) as e:
             call()
-        assert e.value.code == abi.ZERO_EINVAL and "2^41" in str(e.value), k
+        assert e.value.code == abi.ZERO_EINVAL and "2^34" in str(e.value), k
 
 
 def test_quant_sizes():

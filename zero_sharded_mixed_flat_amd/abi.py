@@ -27,7 +27,7 @@ ZERO_EIO = -5
 ZERO_F16 = 1
 ZERO_BF16 = 2
 ZERO_MAX_RANKS = 1024
-ZERO_MAX_ELEMS = 1 << 41
+ZERO_MAX_ELEMS = 1 << 34
 ZERO_FLAG_NONFINITE_GRAD = 1
 ZERO_FLAG_NONFINITE_NORM = 2
 

@@ -551,7 +551,7 @@ int adam_consts(const char* fn, const zero_adam_hparams* hp, AdamConsts* c) {
 int adam_enqueue(const char* fn, float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
                  const AdamConsts& c, const AdamConsts* c_dev, const float* coef_dev, const int32_t* flag,
                  void* param_out, int param_dtype, void* stream) {
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
         return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
     if (coef_dev == nullptr || (addr(coef_dev) & 3) || flag == nullptr || (addr(flag) & 3))
@@ -603,7 +603,7 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
                       int32_t* flag, void* stream) {
     const char* fn = "zero_reduce_shard";
     if (nd < 1 || nd > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": nd must be in [1, 1024]");
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
     if (!pow2_positive(inv_loss_scale))
         return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
@@ -671,7 +671,7 @@ int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
                    int64_t workspace_bytes, int n_sets, const double* extra_sumsq, int n_extra,
                    float max_norm, int32_t* flag, double* norm_out, float* coef_out, void* stream) {
     const char* fn = "zero_grad_norm";
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (n_sets < 1 || n_sets > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": n_sets must be in [1, 1024]");
     if (n_extra < 0 || (n_extra > 0 && (extra_sumsq == nullptr || (addr(extra_sumsq) & 7))))
         return fail(ZERO_EINVAL, std::string(fn) + ": bad extra_sumsq");
@@ -777,7 +777,7 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
         return fail(ZERO_EINVAL, std::string(fn) + ": shards or full NULL, or full misaligned");
     for (int u = unit_begin; u < unit_end; ++u)
         if (plan->units[u].slice_numel > ZERO_MAX_ELEMS)
-            return fail(ZERO_EINVAL, std::string(fn) + ": unit " + std::to_string(u) + "'s slice exceeds 2^41 elements");
+            return fail(ZERO_EINVAL, std::string(fn) + ": unit " + std::to_string(u) + "'s slice exceeds 2^34 elements");
     const int64_t shard_bytes = 2 * plan->shard_numel, full_bytes = 2 * plan->full_numel;
     for (int r = 0; r < owners; ++r) {
         if (shards[r] == nullptr || (addr(shards[r]) & 1))

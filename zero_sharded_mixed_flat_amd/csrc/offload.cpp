@@ -336,7 +336,7 @@ int zero_cpu_adam_step(float* master, float* m, float* v, const void* grad, int 
                        const zero_adam_hparams* hp, float coef, int skip, void* param_out, int param_dtype,
                        int n_threads) {
     const char* fn = "zero_cpu_adam_step";
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (!valid_dtype_h(grad_dtype) || !valid_dtype_h(param_dtype))
         return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
     if (n_threads < 1 || n_threads > kMaxThreads)
@@ -355,7 +355,7 @@ int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_d
                            void* param_dev, int param_dtype, void* staging, int64_t staging_bytes, int n_threads,
                            void* stream) {
     const char* fn = "zero_offload_adam_step";
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (!valid_dtype_h(grad_dtype) || !valid_dtype_h(param_dtype))
         return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
     if (n_threads < 1 || n_threads > kMaxThreads)

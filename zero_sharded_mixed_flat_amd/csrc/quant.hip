@@ -402,7 +402,7 @@ int64_t zero_quant_scale_count(int64_t n) {
 
 int zero_quantize_blocks(const void* x, int dtype, int64_t n, int bits, void* codes, float* scales, void* stream) {
     const char* fn = "zero_quantize_blocks";
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
     if (!valid_bits(bits)) return fail(ZERO_EINVAL, std::string(fn) + ": bits must be 8 or 4");
     if (n == 0) return ok();
@@ -424,7 +424,7 @@ int zero_quantize_blocks(const void* x, int dtype, int64_t n, int bits, void* co
 int zero_dequantize_blocks(const void* codes, const float* scales, int64_t n, int bits, void* y, int dtype,
                            void* stream) {
     const char* fn = "zero_dequantize_blocks";
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^41]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
     if (!valid_bits(bits)) return fail(ZERO_EINVAL, std::string(fn) + ": bits must be 8 or 4");
     if (n == 0) return ok();
@@ -458,7 +458,7 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards, c
     if (unit_begin == unit_end) return ok();
     for (int u = unit_begin; u < unit_end; ++u)
         if (plan->units[u].slice_numel > ZERO_MAX_ELEMS)
-            return fail(ZERO_EINVAL, std::string(fn) + ": unit " + std::to_string(u) + "'s slice exceeds 2^41 elements");
+            return fail(ZERO_EINVAL, std::string(fn) + ": unit " + std::to_string(u) + "'s slice exceeds 2^34 elements");
     const int owners = plan->owners;
     if (code_shards == nullptr || scale_shards == nullptr || full == nullptr || (addr(full) & 15))
         return fail(ZERO_EINVAL, std::string(fn) + ": NULL argument or full not 16-byte aligned");
