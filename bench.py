@@ -193,6 +193,13 @@ def _gather_label(w):
     return ", gather" if w.gather_per_unit else ""
 
 
+def _rows(path):
+    """The rows of a CSV file, read and closed."""
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
 def _short(name):
     name = name.replace("zf::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     return name.replace("void ", "").split("(")[0]
@@ -206,9 +213,8 @@ def summarize_trace(stats_csv, command, bench_log=None):
     output of the profiled bench.py run) it adds bench.py's own HIP-event
     time per launch of the roofline kernel in that same process beside
     rocprofv3's average for that kernel's busiest grid size."""
-    import csv
     from collections import defaultdict
-    rows = list(csv.DictReader(open(stats_csv)))
+    rows = _rows(stats_csv)
     ours = [r for r in rows if "zf::" in r["Name"]]
     other = [r for r in rows if "zf::" not in r["Name"]]
     out = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
@@ -220,7 +226,7 @@ def summarize_trace(stats_csv, command, bench_log=None):
     trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
     if trace_csv != stats_csv and os.path.exists(trace_csv):
         groups = defaultdict(list)
-        for r in csv.DictReader(open(trace_csv)):
+        for r in _rows(trace_csv):
             if "zf::" in r["Kernel_Name"]:
                 groups[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))].append(
                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -235,7 +241,8 @@ def summarize_trace(stats_csv, command, bench_log=None):
 
 def _bench_agreement(bench_log, groups):
     """bench.py's JSON line from the profiled run against the trace of the same run."""
-    lines = [ln for ln in open(bench_log) if ln.startswith('{"metric"')]
+    with open(bench_log) as f:
+        lines = [ln for ln in f if ln.startswith('{"metric"')]
     if not lines:
         raise RuntimeError(f"{bench_log} holds no bench.py result line")
     d = json.loads(lines[-1])
@@ -266,12 +273,11 @@ def summarize_counters(fetch_csv, write_csv, phases, commands):
     workload's phase model (kernel, launches, algorithmic bytes per launch).
     Returns the markdown summary and the traffic entry of every phase kernel.
     """
-    import csv
     from collections import defaultdict
     per = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc = defaultdict(list)
-        for r in csv.DictReader(open(path)):
+        for r in _rows(path):
             if r["Counter_Name"] != counter or "zf::" not in r["Kernel_Name"]:
                 continue
             acc[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))

@@ -52,7 +52,8 @@ def narrow(x, dtype):
     _check(dtype)
     x = np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "f16":
-        return x.astype(np.float16).view(np.uint16)
+        with np.errstate(over="ignore"):       # beyond the fp16 range rounds to infinity (IEEE)
+            return x.astype(np.float16).view(np.uint16)
     return f32_to_bf16_bits(x)
 
 

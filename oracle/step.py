@@ -74,7 +74,8 @@ def reduce_shard(contribs, dtype):
         raise ValueError("contributions must be 1-D and of equal length")
     acc = widen(contribs[0], dtype).copy()
     for c in contribs[1:]:
-        acc = acc + widen(c, dtype)            # float32 + float32 -> float32
+        with np.errstate(over="ignore"):       # an overflow to infinity is reported by the flag
+            acc = acc + widen(c, dtype)        # float32 + float32 -> float32
     mean = acc / np.float32(len(contribs))     # float32 IEEE division
     out = narrow(mean, dtype)
     nonfinite = not all(bool(np.all(is_finite16(c, dtype))) for c in contribs)

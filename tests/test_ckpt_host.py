@@ -12,6 +12,7 @@ Pages cited by short name:
 """
 
 import os
+import pathlib
 
 import numpy as np
 import pytest
@@ -181,23 +182,23 @@ def test_missing_foreign_and_damaged_files(tmp_path):
     assert "parameters" in str(load_error(paths, 0, plan2, ref2.shard_numel))
     # truncated
     damaged = str(tmp_path / "damaged.zck")
-    data = open(paths[1], "rb").read()
-    open(damaged, "wb").write(data[:-4])
+    data = pathlib.Path(paths[1]).read_bytes()
+    pathlib.Path(damaged).write_bytes(data[:-4])
     assert "truncated" in str(load_error([paths[0], damaged] + paths[2:]))
     # one flipped bit in rank 1's m array: rank 1's restore reads it and fails
     header = os.path.getsize(paths[1]) - 3 * 4 * n
     flipped = bytearray(data)
     flipped[header + 4 * n + 4 * 100_000] ^= 0x10                 # m[100000] of a 175000-element shard
-    open(damaged, "wb").write(bytes(flipped))
+    pathlib.Path(damaged).write_bytes(bytes(flipped))
     e = load_error([paths[0], damaged] + paths[2:], rank=1)
     assert e.code == abi.ZERO_EIO and "corrupt" in str(e) and "array 1" in str(e)
     # a damaged header
     flipped = bytearray(data)
     flipped[40] ^= 1
-    open(damaged, "wb").write(bytes(flipped))
+    pathlib.Path(damaged).write_bytes(bytes(flipped))
     assert "corrupt header" in str(load_error([paths[0], damaged] + paths[2:]))
     # not a checkpoint at all
-    open(damaged, "wb").write(b"x" * 4096)
+    pathlib.Path(damaged).write_bytes(b"x" * 4096)
     assert "not a checkpoint" in str(load_error([paths[0], damaged] + paths[2:]))
 
 

@@ -13,7 +13,8 @@ from zero_sharded_mixed_flat_amd import workloads
 
 def test_printed_flat_partitions():
     path = os.path.join(os.path.dirname(__file__), "golden", "pages_flat_partition.csv")
-    rows = [line.strip().split(",") for line in open(path) if line.strip() and not line.startswith("#")]
+    with open(path) as f:
+        rows = [line.strip().split(",") for line in f if line.strip() and not line.startswith("#")]
     assert rows
     for sizes, nd, per_rank, source in rows:
         sizes = [int(x) for x in sizes.split()]

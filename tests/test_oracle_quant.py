@@ -48,7 +48,8 @@ def test_page_experiment(seed):
 
 def _printed():
     path = os.path.join(os.path.dirname(__file__), "golden", "pages_qwz_errors.csv")
-    rows = [line.split(",") for line in open(path) if line.strip() and not line.startswith("#")]
+    with open(path) as f:
+        rows = [line.split(",") for line in f if line.strip() and not line.startswith("#")]
     return [(int(b), blk == "256", float(pct) / 100, float(tol) / 100, src) for b, blk, pct, tol, src in rows]
 
 
