@@ -175,6 +175,25 @@ def test_every_isa_and_thread_count_same_bits(gdt, pdt):
                                       b.view(np.uint32) if b.dtype == np.float32 else b), (isa, threads)
 
 
+@pytest.mark.parametrize("offset", [1, 3, 8])
+def test_misaligned_output_same_bits(offset):
+    # The 16-bit output is streamed when aligned and stored plainly otherwise;
+    # an output that starts `offset` elements into a buffer gives the same bits.
+    hp = HPARAMS["adamw"]
+    n = 100_003
+    g, p, m, v = _inputs(n, "bf16", hp, 31)
+    ref = _run(g, p, m, v, "bf16", "bf16", hp, 2, 0.7, threads=4)
+    for isa in ISAS:
+        abi.zero_cpu_set_isa(isa)
+        tp, tm, tv = (torch.from_numpy(a.copy()) for a in (p, m, v))
+        buf = torch.zeros(n + offset, dtype=torch.int16)
+        abi.zero_cpu_adam_step(tp, tm, tv, torch.from_numpy(g.view(np.int16).copy()), "bf16", n, _abi_hp(hp, 2),
+                               0.7, False, buf[offset:], "bf16", 4)
+        assert np.array_equal(buf[offset:].numpy().view(np.uint16), ref[3]), (isa, offset)
+        assert not buf[:offset].any()
+        assert np.array_equal(tp.numpy().view(np.uint32), ref[0].view(np.uint32))
+
+
 def test_skip_writes_nothing():
     hp = HPARAMS["adam"]
     g, p, m, v = _inputs(1000, "f16", hp, 9)

@@ -118,6 +118,11 @@ __attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) void adam_avx512(
     const __m512i abs_mask = _mm512_set1_epi32(0x7fffffff), inf = _mm512_set1_epi32(0x7f800000),
                   round = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1),
                   qnan = _mm512_set1_epi32(0x7fc0);
+    // The 16-bit output is written once and never read here: streaming stores
+    // skip the read of each line a plain store would do first (2 bytes of host
+    // traffic per element).  They need 32-byte alignment, which a range keeps
+    // once its first element has it, and a fence before the range is done.
+    const bool stream = (reinterpret_cast<uintptr_t>(out + lo) & 31) == 0;
     int64_t i = lo;
     for (; i + 16 <= hi; i += 16) {
         const __m256i graw = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(g16 + i));
@@ -145,8 +150,12 @@ __attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) void adam_avx512(
         } else {
             o = _mm512_cvtps_ph(pp, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
         }
-        _mm256_storeu_si256(reinterpret_cast<__m256i*>(out + i), o);
+        if (stream)
+            _mm256_stream_si256(reinterpret_cast<__m256i*>(out + i), o);
+        else
+            _mm256_storeu_si256(reinterpret_cast<__m256i*>(out + i), o);
     }
+    if (stream) _mm_sfence();
     adam_scalar(c, p, m, v, g16, gdt, out, pdt, i, hi);
 }
 
@@ -164,6 +173,7 @@ __attribute__((target("avx2,f16c"))) void adam_avx2(const HostAdam& c, float* p,
     const __m256i abs_mask = _mm256_set1_epi32(0x7fffffff), inf = _mm256_set1_epi32(0x7f800000),
                   round = _mm256_set1_epi32(0x7fff), one = _mm256_set1_epi32(1),
                   qnan = _mm256_set1_epi32(0x7fc0);
+    const bool stream = (reinterpret_cast<uintptr_t>(out + lo) & 15) == 0;   // as in the AVX-512 path
     int64_t i = lo;
     for (; i + 8 <= hi; i += 8) {
         const __m128i graw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(g16 + i));
@@ -191,8 +201,12 @@ __attribute__((target("avx2,f16c"))) void adam_avx2(const HostAdam& c, float* p,
         } else {
             o = _mm256_cvtps_ph(pp, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
         }
-        _mm_storeu_si128(reinterpret_cast<__m128i*>(out + i), o);
+        if (stream)
+            _mm_stream_si128(reinterpret_cast<__m128i*>(out + i), o);
+        else
+            _mm_storeu_si128(reinterpret_cast<__m128i*>(out + i), o);
     }
+    if (stream) _mm_sfence();
     adam_scalar(c, p, m, v, g16, gdt, out, pdt, i, hi);
 }
 
