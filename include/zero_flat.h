@@ -258,18 +258,22 @@ typedef struct {
 /*
  * zero_adam_step -- the owner updates its fp32 variance, momentum and master,
  * then copies the master to the 16-bit parameter (L18 notes §2.2 step 4;
- * Adam is elementwise, §2.1).  Per element, one IEEE fp32 rounding per
- * operation in this order, no fused multiply-add, correctly rounded division
- * and square root:
- *   g  = f32(grad[i]) * (inv_loss_scale * (*coef_dev))
- *   m  = beta1*m + (1 - beta1)*g
- *   v  = beta2*v + (1 - beta2)*(g*g)
- *   p  = p - lr * ((m * inv_bc1) / (sqrt(v * inv_bc2) + eps) + weight_decay*p)
+ * Adam is elementwise, §2.1).  Per element, in fp64 from the fp32 state, the
+ * 16-bit gradient and the fp32 scalars of zero_adam_consts_fill, one IEEE
+ * fp64 rounding per operation in this order, no fused multiply-add,
+ * correctly rounded division and square root:
+ *   g  = f64(grad[i]) * (inv_loss_scale * (*coef_dev))   (the product is exact)
+ *   m' = beta1*m + (1 - beta1)*g
+ *   v' = beta2*v + (1 - beta2)*(g*g)
+ *   p' = p - lr * ((m' / bc1) / (sqrt(v' / bc2) + eps) + weight_decay*p)
+ *   m, v, p = f32(m'), f32(v'), f32(p')                  (one rounding each)
  *   param_out[i] = round_to_nearest_even_16(p)
- * with the scalars of zero_adam_consts_fill.  zero_cpu_adam_step evaluates
- * the same sequence, so the two give identical bits.  master, m and v are
- * each read once and written once.  If *flag != 0 the kernel writes nothing
- * (the step is skipped).
+ * This is the unsharded data-parallel update itself (L18 notes §2.5: the
+ * sharded run computes what data parallelism computes), so the results do
+ * not depend on how the vector is sharded.  zero_cpu_adam_step evaluates the
+ * same sequence, so the two give identical bits.  master, m and v are each
+ * read once and written once.  If *flag != 0 the kernel writes nothing (the
+ * step is skipped).
  *
  * master, m, v: device fp32, n each, distinct.  grad: device 16-bit
  * (`grad_dtype`), n.  coef_dev: device fp32 (from zero_grad_norm).  flag:
@@ -281,11 +285,11 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
                    const int32_t* flag, void* param_out, int param_dtype, void* stream);
 
 /* The fp32 scalars of one AdamW step, as zero_adam_step derives them from
- * zero_adam_hparams: 1 - beta, the bias corrections bc = 1 - beta^t and their
- * reciprocals inv_bc = 1 / bc, each formed in fp64 and rounded to fp32. */
+ * zero_adam_hparams: 1 - beta and the bias corrections bc = 1 - beta^t, each
+ * formed in fp64 and rounded to fp32. */
 typedef struct {
     float lr, beta1, beta2, one_minus_beta1, one_minus_beta2, eps, weight_decay, inv_loss_scale;
-    float inv_bias_corr1, inv_bias_corr2;
+    float bias_corr1, bias_corr2;
 } zero_adam_consts;
 
 /* Fills *out (host) from hp, with zero_adam_step's checks.  Errors: ZERO_EINVAL. */

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert abi.zero_version() == 10000
+    assert abi.zero_version() == 10100
 
 
 @pytest.mark.parametrize("seed", range(60))

@@ -4,8 +4,8 @@ tests/c_step_driver.c allocates with hipMalloc and calls zero_reduce_shard,
 zero_grad_norm and zero_adam_step; no Python binding and no PyTorch is
 involved in the step.  Its outputs are checked like the binding's: the
 reduced gradient bit for bit against the oracle, the norm and clip multiplier
-within the bounds derived in tolerance.py, and AdamW bit for bit against the
-documented fp32 sequence and within its bounds of the oracle.
+within the bounds in tolerance.py, and AdamW within 1e-9 + 1e-6 relative (one
+16-bit ulp) of the oracle and bit for bit when the clip multipliers agree.
 """
 
 import os
@@ -16,10 +16,9 @@ import numpy as np
 import pytest
 import torch
 
-import fp32_sequence
 from oracle import rounding, step
 from oracle.step import AdamHparams
-from tolerance import adam_ok, coef_ok, norm_ok
+from tolerance import adam_parity, coef_ok, norm_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -77,12 +76,9 @@ def test_c_program_step(driver, tmp_path, dtype, nd, n, std):
     assert np.array_equal(reduced, ref_reduced)
     ref_norm = step.norm_from_sumsq(step.sumsq_exact(ref_reduced, dtype))
     norm_ok(norm, ref_norm, n)
-    coef_ok(coef, step.clip_coef(ref_norm, HP.max_norm))
+    ref_coef = step.clip_coef(ref_norm, HP.max_norm)
+    coef_ok(coef, ref_coef)
     if std == 1e-2:
         assert coef < 1.0
-    # AdamW with the multiplier the device computed
-    seq = fp32_sequence.adamw(master, m, v, reduced, dtype, HP, 1, coef, dtype)
-    for a, b, name in zip(got, seq, ("master", "m", "v", "param")):
-        fp32_sequence.same_bits(a, b, f"C driver {name}")
-    ref = step.adam_update(master, m, v, reduced, dtype, HP, 1, coef, dtype)
-    adam_ok(got, ref, (master, m, v), reduced, dtype, HP, 1, coef, dtype, "C driver")
+    ref = step.adam_update(master, m, v, ref_reduced, dtype, HP, 1, ref_coef, dtype)
+    adam_parity(got, ref, dtype, "C driver", same=coef == ref_coef)

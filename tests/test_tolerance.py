@@ -1,11 +1,10 @@
-"""The derived AdamW tolerances accept the fp32 arithmetic's rounding and
-nothing grossly more: a 16-bit parameter two ulps off fails at ordinary
-magnitudes; the bounds scale with the operands of each update (so a small
-result after cancellation gets an operand-sized bound), and a planted error
-of a few hundred fp32 ulps in an ordinary element fails.  The norm bound
-holds against exact rational sums, even for chains built so that every
-addition loses nearly a whole rounding, and a norm accumulated in fp32 fails
-it."""
+"""The parity bar accepts what it should and nothing more: master, m and v
+within 1e-9 + 1e-6 relative (a planted 1.25e-6 relative error, or 1.1e-9 on a
+tiny value, fails), a 16-bit parameter one ulp off passes and two fail, and
+the bit-identity check catches a single fp32 ulp and an fp32 evaluation of
+the update.  The norm's derived bound holds against exact rational sums,
+even for chains built so that every addition loses nearly a whole rounding,
+and a norm accumulated in fp32 fails it."""
 
 from fractions import Fraction
 
@@ -14,7 +13,8 @@ import pytest
 
 from oracle import rounding, step
 from oracle.step import AdamHparams
-from tolerance import U32, U64, adam_bounds, adam_ok, coef_ok, norm_chain, norm_ok, norm_rel, param16_ok
+from tolerance import (U64, adam_ok, adam_parity, adam_same, coef_ok, norm_chain, norm_ok, norm_rel,
+                       param16_ok, within)
 
 HP = AdamHparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
@@ -32,50 +32,74 @@ def test_param_one_ulp_passes_two_fail_at_ordinary_magnitude(dt):
         param16_ok(x + np.uint16(2), x, dt, "two ulps")
 
 
-def test_param_within_the_master_bound_near_zero():
-    got, ref = _b([3e-10], "bf16"), _b([1e-10], "bf16")
-    param16_ok(got, ref, "bf16", "cancellation", master_bound=np.array([2.5e-10]))
-    with pytest.raises(AssertionError):
-        param16_ok(got, ref, "bf16", "no master bound")
+def test_param_across_zero():
     # fp16 across zero: -0 against the smallest subnormal is one ulp in value
     param16_ok(np.uint16([0x8000]), np.uint16([0x0001]), "f16", "-0 vs the smallest subnormal")
     with pytest.raises(AssertionError):
         param16_ok(np.uint16([0x8001]), np.uint16([0x0001]), "f16", "opposite subnormals")
 
 
-def test_bounds_scale_with_the_operands():
-    # ordinary element: the bound on p is a few dozen ulps of |p|
-    g = _b([1e-4, 1e-4], "bf16")
-    p = np.float32([0.02, 0.003])
-    m = np.float32([1e-5, 1e-4])
-    v = np.float32([1e-8, 1e-16])                # the second: tiny v, a large step that nearly cancels p
-    bp, bm, bv = adam_bounds(p, m, v, g, "bf16", HP, 1, np.float32(1.0))
-    g0 = float(rounding.widen(g, "bf16")[0])
-    a = (0.9 * 1e-5 + 0.1 * g0) / 0.1 / (np.sqrt((0.95 * 1e-8 + 0.05 * g0 * g0) / 0.05) + 1e-8)
-    assert bp[0] == pytest.approx(24 * U32 * (0.02 + 3e-4 * a + 3e-4 * 0.1 * 0.02), rel=1e-3)
-    ref = step.adam_update(p, m, v, g, "bf16", HP, 1, np.float32(1.0), "bf16")
-    step_size = abs(float(p[1]) - float(ref[0][1]))
-    assert step_size > 1e-3                      # the update is large
-    assert bp[1] > 24 * U32 * step_size          # and the bound follows it, not |p'|
-    assert bm[0] <= 8 * U32 * 1e-5 and bv[0] <= 16 * U32 * 1e-8
+def test_within_relative_and_absolute_parts():
+    ref = np.float32([0.02, 1e-12, 0.0, np.inf, np.nan])
+    within(ref, ref, "identical")
+    within(ref + np.float32([0.02 * 7.5e-7, 9e-10, 9e-10, 0, 0]), ref, "inside")
+    for k, d in ((0, 0.02 * 1.25e-6), (1, 1.1e-9), (2, 1.1e-9)):
+        bad = ref.copy()
+        bad[k] += np.float32(d)
+        with pytest.raises(AssertionError):
+            within(bad, ref, f"planted at {k}")
+    with pytest.raises(AssertionError):
+        within(np.float32([0.02, 1e-12, 0.0, 3e38, np.nan]), ref, "inf against a finite value")
 
 
-def test_planted_error_fails():
-    rng = np.random.default_rng(0)
-    n = 1000
+def _update_inputs(n=1000, seed=0):
+    rng = np.random.default_rng(seed)
     g = _b(rng.standard_normal(n) * 1e-4, "bf16")
     p = (rng.standard_normal(n) * 0.02).astype(np.float32)
     m = (rng.standard_normal(n) * 1e-5).astype(np.float32)
     v = np.abs(rng.standard_normal(n) * 1e-8).astype(np.float32)
+    return g, p, m, v
+
+
+def test_planted_error_fails():
+    g, p, m, v = _update_inputs()
     coef = np.float32(0.7)
     ref = step.adam_update(p, m, v, g, "bf16", HP, 2, coef, "bf16")
-    adam_ok(ref, ref, (p, m, v), g, "bf16", HP, 2, coef, "bf16", "identical")
+    adam_parity(ref, ref, "bf16", "identical")
     k = int(np.argmax(np.abs(p)))
     for which in range(3):
         bad = [a.copy() for a in ref]
-        bad[which][k] = np.float32(bad[which][k] * (1 + 300 * U32))
+        x = float(bad[which][k])
+        bad[which][k] = np.float32(x + 1.05 * (1e-9 + 1e-6 * abs(x)))
         with pytest.raises(AssertionError):
-            adam_ok(tuple(bad), ref, (p, m, v), g, "bf16", HP, 2, coef, "bf16", f"planted in output {which}")
+            adam_ok(tuple(bad), ref, "bf16", f"planted in output {which}")
+    # one fp32 ulp passes the bar but not the bit-identity check
+    bad = [a.copy() for a in ref]
+    bad[0][k] = np.nextafter(bad[0][k], np.float32(1))
+    adam_ok(tuple(bad), ref, "bf16", "one fp32 ulp")
+    with pytest.raises(AssertionError):
+        adam_same(tuple(bad), ref, "one fp32 ulp")
+    adam_parity(tuple(bad), ref, "bf16", "one fp32 ulp, different clip multipliers", same=False)
+
+
+def test_bit_identity_catches_an_fp32_evaluation():
+    # The same update evaluated one fp32 operation at a time (not what the
+    # library does) meets the bar on these inputs but not bit identity.
+    g, p, m, v = _update_inputs(20_000, 3)
+    coef = np.float32(0.7)
+    t = 2
+    ref = step.adam_update(p, m, v, g, "bf16", HP, t, coef, "bf16")
+    f = np.float32
+    b1, b2 = f(HP.beta1), f(HP.beta2)
+    bc1, bc2 = (f(x) for x in step.bias_corrections(HP, t))
+    gg = rounding.widen(g, "bf16") * coef
+    m2 = b1 * m + f(1 - float(b1)) * gg
+    v2 = b2 * v + f(1 - float(b2)) * (gg * gg)
+    p2 = p - f(HP.lr) * ((m2 / bc1) / (np.sqrt(v2 / bc2) + f(HP.eps)) + f(HP.weight_decay) * p)
+    fp32 = (p2, m2, v2, rounding.narrow(p2, "bf16"))
+    adam_ok(fp32, ref, "bf16", "fp32 evaluation")
+    with pytest.raises(AssertionError):
+        adam_same(fp32, ref, "fp32 evaluation")
 
 
 def _serial(x):

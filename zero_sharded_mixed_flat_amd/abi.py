@@ -77,7 +77,7 @@ class zero_adam_hparams(ctypes.Structure):
 class zero_adam_consts(ctypes.Structure):
     _fields_ = [(name, ctypes.c_float) for name in (
         "lr", "beta1", "beta2", "one_minus_beta1", "one_minus_beta2", "eps", "weight_decay", "inv_loss_scale",
-        "inv_bias_corr1", "inv_bias_corr2")]
+        "bias_corr1", "bias_corr2")]
 
 
 if not os.path.exists(LIB_PATH):

@@ -309,16 +309,20 @@ __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(
 // ---------------------------------------------------------------------------
 
 struct AdamConsts {
-    float lr, b1, b2, omb1, omb2, eps, wd, inv_s, inv_bc1, inv_bc2;
+    float lr, b1, b2, omb1, omb2, eps, wd, inv_s, bc1, bc2;
 };
 
 // Block b covers quads [b*kAdamTileQuads, (b+1)*kAdamTileQuads) of the body (or
 // elements [b*kAdamTileElems, ...) without `vec`).
 // DEV: the scalars come from device memory (c_dev) instead of the kernel
 // arguments, so a captured graph can replay the launch with new ones.
-// The update is evaluated one fp32 operation at a time, in the order written,
-// with no fused multiply-adds; division and square root round correctly.  The
-// host AdamW evaluates the same sequence, so both give the same bits.
+// The update widens the fp32 state, the 16-bit gradient and the fp32 scalars
+// to fp64 and evaluates it there one operation at a time, in the order
+// written, with no fused multiply-adds and with correctly rounded division
+// and square root; m', v' and p' are each rounded to fp32 once.  That is the
+// unsharded update's own definition, so every output is the one the plain
+// data-parallel step gives (L18 notes §2.5), and the host AdamW, which
+// evaluates the same sequence, gives the same bits.
 template <int GDT, int PDT, bool DEV>
 __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ master,
                                                       float* __restrict__ m,
@@ -331,14 +335,21 @@ __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ ma
 #pragma clang fp contract(off)
     if (*flag != 0) return;  // a skipped step writes nothing
     const AdamConsts c = DEV ? *c_dev : c_arg;
-    const float gs = c.inv_s * *coef_dev;
+    // inv_s is a power of two, so this product is exact and g below is the
+    // 16-bit value times inv_s times coef with a single rounding.
+    const double gs = double(c.inv_s) * double(*coef_dev);
+    const double b1 = c.b1, b2 = c.b2, omb1 = c.omb1, omb2 = c.omb2, lr = c.lr, eps = c.eps, wd = c.wd,
+                 bc1 = c.bc1, bc2 = c.bc2;
 
     auto update = [&](float& p, float& mm, float& vv, uint32_t gb) -> uint32_t {
-        const float g = widen<GDT>(gb) * gs;
-        mm = c.b1 * mm + c.omb1 * g;
-        vv = c.b2 * vv + c.omb2 * (g * g);
-        const float denom = sqrtf(vv * c.inv_bc2) + c.eps;
-        p = p - c.lr * ((mm * c.inv_bc1) / denom + c.wd * p);
+        const double g = double(widen<GDT>(gb)) * gs;
+        const double m2 = b1 * double(mm) + omb1 * g;
+        const double v2 = b2 * double(vv) + omb2 * (g * g);
+        const double p0 = double(p);
+        const double p2 = p0 - lr * ((m2 / bc1) / (sqrt(v2 / bc2) + eps) + wd * p0);
+        mm = static_cast<float>(m2);
+        vv = static_cast<float>(v2);
+        p = static_cast<float>(p2);
         return narrow<PDT>(p);
     };
     auto update4 = [&](f4& p, f4& mm, f4& vv, const u2& g) -> u2 {
@@ -538,11 +549,10 @@ int adam_consts(const char* fn, const zero_adam_hparams* hp, AdamConsts* c) {
     c->eps = hp->eps;
     c->wd = hp->weight_decay;
     c->inv_s = hp->inv_loss_scale;
-    const float bc1 = float(1.0 - std::pow(double(hp->beta1), double(hp->step)));
-    const float bc2 = float(1.0 - std::pow(double(hp->beta2), double(hp->step)));
-    if (!(bc1 > 0.0f) || !(bc2 > 0.0f)) return fail(ZERO_EINVAL, std::string(fn) + ": bias correction is zero");
-    c->inv_bc1 = float(1.0 / double(bc1));
-    c->inv_bc2 = float(1.0 / double(bc2));
+    c->bc1 = float(1.0 - std::pow(double(hp->beta1), double(hp->step)));
+    c->bc2 = float(1.0 - std::pow(double(hp->beta2), double(hp->step)));
+    if (!(c->bc1 > 0.0f) || !(c->bc2 > 0.0f))
+        return fail(ZERO_EINVAL, std::string(fn) + ": bias correction is zero");
     return ZERO_OK;
 }
 

@@ -7,11 +7,14 @@
 // where a multi-threaded, vectorised Adam updates them; each step sends the
 // gradient to the host and the 16-bit parameters back (L18 notes §4.4).
 //
-// Arithmetic: the same fp32 operation sequence as the GPU kernel, in IEEE
-// single precision with no fused multiply-add, so the AVX-512, AVX2 and scalar
-// paths give identical bits on every x86-64 host.  fp16 conversions use the
-// F16C instructions on the vector paths (round to nearest even) and an exact
-// software conversion on the scalar path; bf16 uses integer rounding.
+// Arithmetic: the GPU kernel's sequence -- the fp32 state, the 16-bit gradient
+// and the fp32 scalars widened to fp64, one IEEE fp64 rounding per operation
+// with no fused multiply-add, correctly rounded division and square root, and
+// one rounding of m', v' and p' to fp32 -- so the AVX-512, AVX2 and scalar
+// paths give identical bits on every x86-64 host, and the same bits as the
+// GPU.  fp16 conversions use the F16C instructions on the vector paths (round
+// to nearest even) and an exact software conversion on the scalar path; bf16
+// uses integer rounding.
 //
 // Pages cited by short name:
 //   L18 notes  CMU 11-868 Lecture 18 notes, "Memory Optimization in Distributed Training: ZeRO" (semidirectx.com)
@@ -33,8 +36,11 @@
 namespace zf {
 namespace {
 
+// The step's scalars widened to fp64 (exactly: each is an fp32 value; gs is
+// inv_loss_scale times the clip multiplier, exact because the former is a
+// power of two).
 struct HostAdam {
-    float lr, b1, b2, omb1, omb2, eps, wd, gs, inv_bc1, inv_bc2;
+    double lr, b1, b2, omb1, omb2, eps, wd, gs, bc1, bc2;
 };
 
 // ---------------------------------------------------------------------------
@@ -92,84 +98,85 @@ inline uint16_t narrow_scalar(float x, int dt) {
 inline void adam_scalar(const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt,
                         uint16_t* out, int pdt, int64_t lo, int64_t hi) {
     for (int64_t i = lo; i < hi; ++i) {
-        const float g = widen_scalar(g16[i], gdt) * c.gs;
-        const float mm = c.b1 * m[i] + c.omb1 * g;
-        const float vv = c.b2 * v[i] + c.omb2 * (g * g);
-        const float denom = std::sqrt(vv * c.inv_bc2) + c.eps;
-        const float pp = p[i] - c.lr * ((mm * c.inv_bc1) / denom + c.wd * p[i]);
-        m[i] = mm;
-        v[i] = vv;
-        p[i] = pp;
-        out[i] = narrow_scalar(pp, pdt);
+        const double g = double(widen_scalar(g16[i], gdt)) * c.gs;
+        const double m2 = c.b1 * double(m[i]) + c.omb1 * g;
+        const double v2 = c.b2 * double(v[i]) + c.omb2 * (g * g);
+        const double p0 = double(p[i]);
+        const double p2 = p0 - c.lr * ((m2 / c.bc1) / (std::sqrt(v2 / c.bc2) + c.eps) + c.wd * p0);
+        m[i] = float(m2);
+        v[i] = float(v2);
+        p[i] = float(p2);
+        out[i] = narrow_scalar(p[i], pdt);
     }
 }
 
 // ---------------------------------------------------------------------------
-// AVX-512: 16 elements per iteration
+// AVX-512: 8 elements (one register of fp64) per iteration
 // ---------------------------------------------------------------------------
 
-__attribute__((target("avx512f,avx512bw,avx512vl,f16c"))) void adam_avx512(
+__attribute__((target("avx512f,avx512bw,avx512vl,avx2,f16c"))) void adam_avx512(
     const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt, uint16_t* out, int pdt,
     int64_t lo, int64_t hi) {
-    const __m512 b1 = _mm512_set1_ps(c.b1), b2 = _mm512_set1_ps(c.b2), omb1 = _mm512_set1_ps(c.omb1),
-                 omb2 = _mm512_set1_ps(c.omb2), eps = _mm512_set1_ps(c.eps), lr = _mm512_set1_ps(c.lr),
-                 wd = _mm512_set1_ps(c.wd), gs = _mm512_set1_ps(c.gs), ibc1 = _mm512_set1_ps(c.inv_bc1),
-                 ibc2 = _mm512_set1_ps(c.inv_bc2);
-    const __m512i abs_mask = _mm512_set1_epi32(0x7fffffff), inf = _mm512_set1_epi32(0x7f800000),
-                  round = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1),
-                  qnan = _mm512_set1_epi32(0x7fc0);
+    const __m512d b1 = _mm512_set1_pd(c.b1), b2 = _mm512_set1_pd(c.b2), omb1 = _mm512_set1_pd(c.omb1),
+                  omb2 = _mm512_set1_pd(c.omb2), eps = _mm512_set1_pd(c.eps), lr = _mm512_set1_pd(c.lr),
+                  wd = _mm512_set1_pd(c.wd), gs = _mm512_set1_pd(c.gs), bc1 = _mm512_set1_pd(c.bc1),
+                  bc2 = _mm512_set1_pd(c.bc2);
+    const __m256i abs_mask = _mm256_set1_epi32(0x7fffffff), inf = _mm256_set1_epi32(0x7f800000),
+                  round = _mm256_set1_epi32(0x7fff), one = _mm256_set1_epi32(1),
+                  qnan = _mm256_set1_epi32(0x7fc0);
     // The 16-bit output is written once and never read here: streaming stores
     // skip the read of each line a plain store would do first (2 bytes of host
-    // traffic per element).  They need 32-byte alignment, which a range keeps
+    // traffic per element).  They need 16-byte alignment, which a range keeps
     // once its first element has it, and a fence before the range is done.
-    const bool stream = (reinterpret_cast<uintptr_t>(out + lo) & 31) == 0;
+    const bool stream = (reinterpret_cast<uintptr_t>(out + lo) & 15) == 0;
     int64_t i = lo;
-    for (; i + 16 <= hi; i += 16) {
-        const __m256i graw = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(g16 + i));
-        __m512 g = gdt == ZERO_BF16 ? _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(graw), 16))
-                                    : _mm512_cvtph_ps(graw);
-        g = _mm512_mul_ps(g, gs);
-        const __m512 pv = _mm512_loadu_ps(p + i);
-        const __m512 mm = _mm512_add_ps(_mm512_mul_ps(b1, _mm512_loadu_ps(m + i)), _mm512_mul_ps(omb1, g));
-        const __m512 vv =
-            _mm512_add_ps(_mm512_mul_ps(b2, _mm512_loadu_ps(v + i)), _mm512_mul_ps(omb2, _mm512_mul_ps(g, g)));
-        const __m512 denom = _mm512_add_ps(_mm512_sqrt_ps(_mm512_mul_ps(vv, ibc2)), eps);
-        const __m512 upd = _mm512_add_ps(_mm512_div_ps(_mm512_mul_ps(mm, ibc1), denom), _mm512_mul_ps(wd, pv));
-        const __m512 pp = _mm512_sub_ps(pv, _mm512_mul_ps(lr, upd));
-        _mm512_storeu_ps(m + i, mm);
-        _mm512_storeu_ps(v + i, vv);
-        _mm512_storeu_ps(p + i, pp);
-        __m256i o;
+    for (; i + 8 <= hi; i += 8) {
+        const __m128i graw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(g16 + i));
+        const __m256 g32 = gdt == ZERO_BF16 ? _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(graw), 16))
+                                            : _mm256_cvtph_ps(graw);
+        const __m512d g = _mm512_mul_pd(_mm512_cvtps_pd(g32), gs);
+        const __m512d p0 = _mm512_cvtps_pd(_mm256_loadu_ps(p + i));
+        const __m512d m2 =
+            _mm512_add_pd(_mm512_mul_pd(b1, _mm512_cvtps_pd(_mm256_loadu_ps(m + i))), _mm512_mul_pd(omb1, g));
+        const __m512d v2 = _mm512_add_pd(_mm512_mul_pd(b2, _mm512_cvtps_pd(_mm256_loadu_ps(v + i))),
+                                         _mm512_mul_pd(omb2, _mm512_mul_pd(g, g)));
+        const __m512d denom = _mm512_add_pd(_mm512_sqrt_pd(_mm512_div_pd(v2, bc2)), eps);
+        const __m512d upd = _mm512_add_pd(_mm512_div_pd(_mm512_div_pd(m2, bc1), denom), _mm512_mul_pd(wd, p0));
+        const __m256 pf = _mm512_cvtpd_ps(_mm512_sub_pd(p0, _mm512_mul_pd(lr, upd)));
+        _mm256_storeu_ps(m + i, _mm512_cvtpd_ps(m2));
+        _mm256_storeu_ps(v + i, _mm512_cvtpd_ps(v2));
+        _mm256_storeu_ps(p + i, pf);
+        __m128i o;
         if (pdt == ZERO_BF16) {
-            const __m512i u = _mm512_castps_si512(pp);
-            const __mmask16 nan = _mm512_cmpgt_epi32_mask(_mm512_and_si512(u, abs_mask), inf);
-            const __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u, 16), one);
-            __m512i r = _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(u, round), lsb), 16);
-            r = _mm512_mask_mov_epi32(r, nan, qnan);
-            o = _mm512_cvtepi32_epi16(r);
+            const __m256i u = _mm256_castps_si256(pf);
+            const __mmask8 nan = _mm256_cmpgt_epi32_mask(_mm256_and_si256(u, abs_mask), inf);
+            const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), one);
+            __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, round), lsb), 16);
+            r = _mm256_mask_mov_epi32(r, nan, qnan);
+            o = _mm256_cvtepi32_epi16(r);
         } else {
-            o = _mm512_cvtps_ph(pp, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+            o = _mm256_cvtps_ph(pf, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
         }
         if (stream)
-            _mm256_stream_si256(reinterpret_cast<__m256i*>(out + i), o);
+            _mm_stream_si128(reinterpret_cast<__m128i*>(out + i), o);
         else
-            _mm256_storeu_si256(reinterpret_cast<__m256i*>(out + i), o);
+            _mm_storeu_si128(reinterpret_cast<__m128i*>(out + i), o);
     }
     if (stream) _mm_sfence();
     adam_scalar(c, p, m, v, g16, gdt, out, pdt, i, hi);
 }
 
 // ---------------------------------------------------------------------------
-// AVX2: 8 elements per iteration
+// AVX2: 8 elements (two registers of fp64) per iteration
 // ---------------------------------------------------------------------------
 
 __attribute__((target("avx2,f16c"))) void adam_avx2(const HostAdam& c, float* p, float* m, float* v,
                                                      const uint16_t* g16, int gdt, uint16_t* out, int pdt,
                                                      int64_t lo, int64_t hi) {
-    const __m256 b1 = _mm256_set1_ps(c.b1), b2 = _mm256_set1_ps(c.b2), omb1 = _mm256_set1_ps(c.omb1),
-                 omb2 = _mm256_set1_ps(c.omb2), eps = _mm256_set1_ps(c.eps), lr = _mm256_set1_ps(c.lr),
-                 wd = _mm256_set1_ps(c.wd), gs = _mm256_set1_ps(c.gs), ibc1 = _mm256_set1_ps(c.inv_bc1),
-                 ibc2 = _mm256_set1_ps(c.inv_bc2);
+    const __m256d b1 = _mm256_set1_pd(c.b1), b2 = _mm256_set1_pd(c.b2), omb1 = _mm256_set1_pd(c.omb1),
+                  omb2 = _mm256_set1_pd(c.omb2), eps = _mm256_set1_pd(c.eps), lr = _mm256_set1_pd(c.lr),
+                  wd = _mm256_set1_pd(c.wd), gs = _mm256_set1_pd(c.gs), bc1 = _mm256_set1_pd(c.bc1),
+                  bc2 = _mm256_set1_pd(c.bc2);
     const __m256i abs_mask = _mm256_set1_epi32(0x7fffffff), inf = _mm256_set1_epi32(0x7f800000),
                   round = _mm256_set1_epi32(0x7fff), one = _mm256_set1_epi32(1),
                   qnan = _mm256_set1_epi32(0x7fc0);
@@ -177,29 +184,37 @@ __attribute__((target("avx2,f16c"))) void adam_avx2(const HostAdam& c, float* p,
     int64_t i = lo;
     for (; i + 8 <= hi; i += 8) {
         const __m128i graw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(g16 + i));
-        __m256 g = gdt == ZERO_BF16 ? _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(graw), 16))
-                                    : _mm256_cvtph_ps(graw);
-        g = _mm256_mul_ps(g, gs);
-        const __m256 pv = _mm256_loadu_ps(p + i);
-        const __m256 mm = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(m + i)), _mm256_mul_ps(omb1, g));
-        const __m256 vv =
-            _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(v + i)), _mm256_mul_ps(omb2, _mm256_mul_ps(g, g)));
-        const __m256 denom = _mm256_add_ps(_mm256_sqrt_ps(_mm256_mul_ps(vv, ibc2)), eps);
-        const __m256 upd = _mm256_add_ps(_mm256_div_ps(_mm256_mul_ps(mm, ibc1), denom), _mm256_mul_ps(wd, pv));
-        const __m256 pp = _mm256_sub_ps(pv, _mm256_mul_ps(lr, upd));
-        _mm256_storeu_ps(m + i, mm);
-        _mm256_storeu_ps(v + i, vv);
-        _mm256_storeu_ps(p + i, pp);
+        const __m256 g32 = gdt == ZERO_BF16 ? _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(graw), 16))
+                                            : _mm256_cvtph_ps(graw);
+        __m128 ph[2];
+        for (int h = 0; h < 2; ++h) {
+            const int64_t j = i + 4 * h;
+            const __m128 gh = h ? _mm256_extractf128_ps(g32, 1) : _mm256_castps256_ps128(g32);
+            const __m256d g = _mm256_mul_pd(_mm256_cvtps_pd(gh), gs);
+            const __m256d p0 = _mm256_cvtps_pd(_mm_loadu_ps(p + j));
+            const __m256d m2 =
+                _mm256_add_pd(_mm256_mul_pd(b1, _mm256_cvtps_pd(_mm_loadu_ps(m + j))), _mm256_mul_pd(omb1, g));
+            const __m256d v2 = _mm256_add_pd(_mm256_mul_pd(b2, _mm256_cvtps_pd(_mm_loadu_ps(v + j))),
+                                             _mm256_mul_pd(omb2, _mm256_mul_pd(g, g)));
+            const __m256d denom = _mm256_add_pd(_mm256_sqrt_pd(_mm256_div_pd(v2, bc2)), eps);
+            const __m256d upd =
+                _mm256_add_pd(_mm256_div_pd(_mm256_div_pd(m2, bc1), denom), _mm256_mul_pd(wd, p0));
+            ph[h] = _mm256_cvtpd_ps(_mm256_sub_pd(p0, _mm256_mul_pd(lr, upd)));
+            _mm_storeu_ps(m + j, _mm256_cvtpd_ps(m2));
+            _mm_storeu_ps(v + j, _mm256_cvtpd_ps(v2));
+            _mm_storeu_ps(p + j, ph[h]);
+        }
+        const __m256 pf = _mm256_set_m128(ph[1], ph[0]);
         __m128i o;
         if (pdt == ZERO_BF16) {
-            const __m256i u = _mm256_castps_si256(pp);
+            const __m256i u = _mm256_castps_si256(pf);
             const __m256i nan = _mm256_cmpgt_epi32(_mm256_and_si256(u, abs_mask), inf);
             const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), one);
             __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, round), lsb), 16);
             r = _mm256_blendv_epi8(r, qnan, nan);
             o = _mm_packus_epi32(_mm256_castsi256_si128(r), _mm256_extracti128_si256(r, 1));
         } else {
-            o = _mm256_cvtps_ph(pp, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+            o = _mm256_cvtps_ph(pf, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
         }
         if (stream)
             _mm_stream_si128(reinterpret_cast<__m128i*>(out + i), o);
@@ -305,9 +320,9 @@ int make_consts(const char* fn, const zero_adam_hparams* hp, float coef, HostAda
     c->omb2 = float(1.0 - double(hp->beta2));
     c->eps = hp->eps;
     c->wd = hp->weight_decay;
-    c->gs = hp->inv_loss_scale * coef;
-    c->inv_bc1 = float(1.0 / double(bc1));
-    c->inv_bc2 = float(1.0 / double(bc2));
+    c->gs = double(hp->inv_loss_scale) * double(coef);
+    c->bc1 = bc1;
+    c->bc2 = bc2;
     return ZERO_OK;
 }
 
@@ -426,7 +441,7 @@ int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_d
     }
     if (rc == ZERO_OK && !(std::isfinite(*coef_h) && *coef_h > 0.0f))
         rc = fail(ZERO_EINVAL, std::string(fn) + ": the clip multiplier on the device is not finite and positive");
-    if (rc == ZERO_OK) c.gs = hp->inv_loss_scale * *coef_h;
+    if (rc == ZERO_OK) c.gs = double(hp->inv_loss_scale) * double(*coef_h);
 
     // Chunk k: gradient in (slot k%2) -> host AdamW -> parameters out (slot k%2).
     // The copy of chunk k+1 is queued before chunk k is updated, and a slot's
