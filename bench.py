@@ -151,7 +151,7 @@ def cpu_baseline(run, budget_s=12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{threads} threads, each on its own {chunk}-element chunk of this workload's inputs "
-                  f"({sum(counts) // chunk} chunk steps: reduce over {w.nd} ranks, exact norm, "
+                  f"({sum(counts) // chunk} chunk steps: {_reduce_label(w)}, exact norm, "
                   f"AdamW{_gather_label(w)}), numpy",
         "seconds": round(dt, 3),
     }, parity
@@ -207,6 +207,12 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def _reduce_label(w):
+    if w.pre_reduced:
+        return "gradient arrives reduced (no reduce)"
+    return f"reduce over {w.nd} ranks"
 
 
 def _gather_label(w):
@@ -553,13 +559,15 @@ def main():
         run.t += 1
     torch.cuda.synchronize()
     del lead
+    per_step = {p: [] for p in phases}
     for ev in events:
         step_ms.append(ev["step"][0].elapsed_time(ev["step"][1]))
         for p in phases:
             if (p == "reduce" and w.pre_reduced or p == "gather" and run.shards is None
                     or p == "quantize" and run.codes is None):
                 continue
-            acc[p] += ev[p][0].elapsed_time(ev[p][1])
+            per_step[p].append(ev[p][0].elapsed_time(ev[p][1]))
+            acc[p] += per_step[p][-1]
     kern_ms = {p: acc[p] / args.steps for p in phases}
 
     # Plain-copy ceiling in the same run: the gather kernel on a one-unit,
@@ -597,6 +605,10 @@ def main():
     dom_launch_ms = kern_ms[dom] / phase_model[dom]["launches"]
     dom_bytes = phase_model[dom]["bytes_per_launch"]
     dom_gbs = dom_bytes / (dom_launch_ms * 1e-3) / 1e9
+    # Spread of the dominant kernel over the timed steps (GB/s per launch).
+    dom_steps = sorted(dom_bytes / (t / phase_model[dom]["launches"] * 1e-3) / 1e9 for t in per_step[dom])
+    dom_spread = {"min": dom_steps[0], "median": dom_steps[len(dom_steps) // 2], "max": dom_steps[-1],
+                  "steps": len(dom_steps)}
     traffic = measured_traffic(name, phase_model[dom]["kernel"])
     roofline = {"bound": "hbm", "peak": HBM_PEAK_GBS, "peak_source": "MI355X published HBM3E bandwidth"}
     offload = None
@@ -626,7 +638,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # arithmetic: the reduce adds in fp32, the norm and AdamW compute in fp64
+        "dtype": "f64" if w.pre_reduced else "f32+f64",
         "data": "synthetic",
         "config": {
             "workload": name, "psi": w.psi, "nd": w.nd, "zero_stage": w.stage, "rank": w.rank,
@@ -653,6 +666,8 @@ def main():
             "peak_source": roofline["peak_source"],
             "unit": "GB/s",
             "frac": dom_gbs / roofline["peak"],
+            "achieved_per_step": dom_spread,
+            "frac_per_step": {k: (v / roofline["peak"] if k != "steps" else v) for k, v in dom_spread.items()},
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dom_bytes,
             "launch_ms": dom_launch_ms,

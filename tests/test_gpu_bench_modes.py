@@ -41,6 +41,8 @@ def _step_line(d):
     rf = d["roofline"]
     assert {"bound", "achieved", "peak", "unit", "frac", "traffic"} <= set(rf)
     assert rf["achieved"] > 0 and rf["peak"] == 8000.0 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    sp = rf["achieved_per_step"]
+    assert 0 < sp["min"] <= sp["median"] <= sp["max"] and sp["steps"] == d["steps"]
     assert d["step_flag"] == 0
 
 

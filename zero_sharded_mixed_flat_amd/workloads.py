@@ -141,7 +141,9 @@ WORKLOADS = {
     ]
 }
 
-BENCH_DEFAULT = "llama3_8b_nd8_z2"
+# The largest configuration that fits one GPU: the 175e9-parameter, 16-rank
+# owner update (10.94e9 owned elements, about 175 GB resident in HBM).
+BENCH_DEFAULT = "gpt3_175b_nd16_z1"
 
 
 def get(name):
