@@ -27,7 +27,8 @@
  *   the runtime); those functions say which outputs are then unusable.
  * - Device buffers are owned by the caller (allocated with any allocator,
  *   e.g. PyTorch).  The library allocates no device memory; kernels that need
- *   scratch use the caller's workspace (zero_workspace_bytes).
+ *   scratch use the caller's workspace (zero_workspace_bytes), except
+ *   zero_grad_norm_noalloc, whose scratch is a static device array.
  * - Device work is enqueued asynchronously on `stream` (a hipStream_t passed
  *   as void*; NULL = the null stream) on the current HIP device.  Results are
  *   valid once the stream reaches that point.  Calls are re-entrant; calls
@@ -240,6 +241,35 @@ int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale,
                    void* workspace, int64_t workspace_bytes, int n_sets,
                    const double* extra_sumsq, int n_extra, float max_norm, int32_t* flag,
                    double* norm_out, float* coef_out, void* stream);
+
+/* Largest n of zero_grad_norm_noalloc, and the size of its static scratch. */
+#define ZERO_NOALLOC_MAX_ELEMS (INT64_C(1) << 34)
+#define ZERO_NOALLOC_SCRATCH_BYTES (16384 + 8 * (ZERO_NOALLOC_MAX_ELEMS / 2048))
+
+/*
+ * zero_grad_norm_noalloc -- zero_grad_norm on an already-reduced gradient
+ * (grad not NULL, one set), for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Instead of a caller's workspace it uses a static device array
+ * of ZERO_NOALLOC_SCRATCH_BYTES (about 64 MiB) that each GPU the library runs
+ * on holds until the process ends; the call itself allocates nothing.  Same
+ * kernels, same summation tree, so norm_out, coef_out and the flag are
+ * bitwise those of zero_grad_norm with n_sets = 1.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * partial sums (nothing in it needs clearing: each call writes every partial
+ * it reads).  Calls that overlap on one GPU -- on different streams, or from
+ * different threads -- race; order them on one stream.  The first call on a
+ * device resolves the array's address on that device (hipGetSymbolAddress,
+ * with that device current); make it outside graph capture.
+ *
+ * grad: device 16-bit (`dtype`), n; 0 <= n <= ZERO_NOALLOC_MAX_ELEMS.  Other
+ * arguments and errors as zero_grad_norm (ZERO_EINVAL for a NULL grad or a
+ * larger n, before anything is enqueued).
+ */
+int zero_grad_norm_noalloc(const void* grad, int64_t n, int dtype, float inv_loss_scale,
+                           const double* extra_sumsq, int n_extra, float max_norm, int32_t* flag,
+                           double* norm_out, float* coef_out, void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* a3: fused Adam(W) on the owned fp32 state, writing the 16-bit parameter */

@@ -192,6 +192,18 @@ def test_grad_norm_rejects():
             abi.zero_grad_norm(**args)
 
 
+def test_grad_norm_noalloc_rejects():
+    # checked before any HIP call: a NULL gradient, n outside [0, 2^34]
+    base = dict(grad=B, n=100, dtype=1, inv_loss_scale=1.0, extra_sumsq=None, n_extra=0, max_norm=1.0, flag=F,
+                norm_out=F + 8, coef_out=F + 16, stream=0)
+    for bad in (dict(grad=None), dict(n=abi.ZERO_NOALLOC_MAX_ELEMS + 1), dict(n=-1)):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_grad_norm_noalloc(**dict(base, **bad))
+        assert e.value.code == abi.ZERO_EINVAL, bad
+    # its static scratch is exactly a one-set workspace at the largest n
+    assert abi.ZERO_NOALLOC_SCRATCH_BYTES == abi.zero_workspace_bytes(abi.ZERO_NOALLOC_MAX_ELEMS, 1)
+
+
 def test_gather_rejects():
     plan = abi.Plan([1000, 1000], 4, 3, 8)
     base = dict(plan=plan, shards=[A + i * 4096 for i in range(4)], unit_begin=0, unit_end=2, dtype=1,

@@ -40,6 +40,7 @@ EXPORTED = (
     "zero_quant_code_bytes", "zero_quant_scale_count", "zero_quantize_blocks", "zero_dequantize_blocks",
     "zero_gather_dequant", "zero_cpu_adam_step", "zero_offload_adam_step", "zero_cpu_isa", "zero_cpu_set_isa",
     "zero_plan_reshard", "zero_ckpt_save", "zero_ckpt_load", "zero_adam_consts_fill", "zero_adam_step_consts",
+    "zero_grad_norm_noalloc",
 )
 ZERO_QBLOCK = 256
 ZERO_CPU_SCALAR = 0
@@ -50,6 +51,8 @@ ZERO_LOC_DEVICE = 0
 ZERO_LOC_HOST = 1
 ZERO_CKPT_BLOCK = 262144
 ZERO_CKPT_MIN_STAGING = 2 * 4 * ZERO_CKPT_BLOCK
+ZERO_NOALLOC_MAX_ELEMS = 1 << 34
+ZERO_NOALLOC_SCRATCH_BYTES = 16384 + 8 * (ZERO_NOALLOC_MAX_ELEMS // 2048)
 
 
 class ZeroError(RuntimeError):
@@ -106,6 +109,7 @@ _sig = {
                                _P]),
     "zero_grad_norm": (_I, [_P, _I64, _I, ctypes.c_float, _P, _I64, _I, _P, _I, ctypes.c_float, _P, _P,
                             _P, _P]),
+    "zero_grad_norm_noalloc": (_I, [_P, _I64, _I, ctypes.c_float, _P, _I, ctypes.c_float, _P, _P, _P, _P]),
     "zero_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
                             _P]),
     "zero_gather_params": (_I, [_P, ctypes.POINTER(_P), _I, _I, _I, _P, _P, _I64, _P]),
@@ -368,6 +372,18 @@ def zero_grad_norm(grad, n, dtype, inv_loss_scale, workspace, n_sets, extra_sums
     _check(lib.zero_grad_norm(_ptr(grad), int(n), dt, float(inv_loss_scale), _ptr(workspace), wb,
                               int(n_sets), _ptr(extra_sumsq), int(n_extra), float(max_norm), _ptr(flag),
                               _ptr(norm_out), _ptr(coef_out), _stream(stream)))
+
+
+def zero_grad_norm_noalloc(grad, n, dtype, inv_loss_scale, extra_sumsq, n_extra, max_norm, flag, norm_out,
+                           coef_out, stream=None):
+    _need(grad, 2 * n, "grad")
+    _need(extra_sumsq, 8 * n_extra, "extra_sumsq")
+    for t, b, what in ((flag, 4, "flag"), (norm_out, 8, "norm_out"), (coef_out, 4, "coef_out")):
+        _need(t, b, what)
+    dt = _dtype(dtype) if grad is not None else 0
+    _check(lib.zero_grad_norm_noalloc(_ptr(grad), int(n), dt, float(inv_loss_scale), _ptr(extra_sumsq),
+                                      int(n_extra), float(max_norm), _ptr(flag), _ptr(norm_out), _ptr(coef_out),
+                                      _stream(stream)))
 
 
 def adam_hparams(lr, beta1, beta2, eps, weight_decay, inv_loss_scale, step):

@@ -39,6 +39,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <utility>
@@ -601,6 +602,118 @@ int adam_enqueue(const char* fn, float* master, float* m, float* v, const void* 
     return hip_status(e, fn);
 }
 
+// zero_grad_norm's checks and launches, on a workspace the caller passes or
+// on the static scratch (fn names the entry point in error messages).
+int grad_norm_enqueue(const char* fn, const void* grad, int64_t n, int dtype, float inv_loss_scale,
+                      void* workspace, int64_t workspace_bytes, int n_sets, const double* extra_sumsq,
+                      int n_extra, float max_norm, int32_t* flag, double* norm_out, float* coef_out,
+                      void* stream) {
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
+    if (n_sets < 1 || n_sets > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": n_sets must be in [1, 1024]");
+    if (n_extra < 0 || (n_extra > 0 && (extra_sumsq == nullptr || (addr(extra_sumsq) & 7))))
+        return fail(ZERO_EINVAL, std::string(fn) + ": bad extra_sumsq");
+    if (!std::isfinite(max_norm)) return fail(ZERO_EINVAL, std::string(fn) + ": max_norm must be finite");
+    if (workspace == nullptr || (addr(workspace) & 7))
+        return fail(ZERO_EINVAL, std::string(fn) + ": workspace NULL or not 8-byte aligned");
+    if (workspace_bytes < zero_workspace_bytes(n, n_sets))
+        return fail(ZERO_EINVAL, std::string(fn) + ": workspace too small");
+    if (flag == nullptr || (addr(flag) & 3) || norm_out == nullptr || (addr(norm_out) & 7) ||
+        coef_out == nullptr || (addr(coef_out) & 3))
+        return fail(ZERO_EINVAL, std::string(fn) + ": flag, norm_out or coef_out NULL or misaligned");
+    if (grad != nullptr) {
+        if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
+        if (!pow2_positive(inv_loss_scale))
+            return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
+        if (n > 0 && (addr(grad) & 1)) return fail(ZERO_EINVAL, std::string(fn) + ": grad misaligned");
+        if (overlaps(grad, 2 * n, workspace, workspace_bytes))
+            return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps grad");
+    }
+    if (overlaps(norm_out, 8, workspace, workspace_bytes) || overlaps(coef_out, 4, workspace, workspace_bytes) ||
+        overlaps(flag, 4, workspace, workspace_bytes) || overlaps(norm_out, 8, coef_out, 4))
+        return fail(ZERO_EALIAS, std::string(fn) + ": outputs overlap");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t blocks = partial_blocks(n);
+    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kPartialsOffset);
+    double* level2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + kTableBytes);
+    if (grad != nullptr && n > 0) {
+        const void* p16[1] = {grad};
+        const Span sp = make_span(n, p16, 1, nullptr, 0);
+        const uint16_t* g16 = static_cast<const uint16_t*>(grad);
+        const dim3 grid{unsigned(ceil_div(blocks, int64_t(kSumsqWaves) * kSumsqRangesPerWave))};
+        const hipError_t e =
+            dtype == ZERO_F16
+                ? launch(sumsq_kernel<ZERO_F16>, grid, dim3(kSumsqBlock), s, g16, sp, inv_loss_scale, blocks,
+                         partials, flag)
+                : launch(sumsq_kernel<ZERO_BF16>, grid, dim3(kSumsqBlock), s, g16, sp, inv_loss_scale, blocks,
+                         partials, flag);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    // With n = 0 every partial sum is zero by definition: none is read, so an
+    // empty gradient needs no partials pass and no earlier launch.
+    const int64_t count = n > 0 ? int64_t(n_sets) * blocks : 0;
+    const double* values = partials;
+    int64_t n_values = count;
+    if (count > kSingleStageMax) {
+        const int64_t groups = std::min<int64_t>(kLevel2Max, ceil_div(count, kStageChunkMin));
+        const int64_t chunk = ceil_div(count, groups);
+        const int64_t used = ceil_div(count, chunk);
+        const hipError_t e = launch(fold_kernel, dim3(unsigned(used)), dim3(kStageBlock), s, partials, count,
+                                    chunk, level2);
+        if (e != hipSuccess) return hip_status(e, fn);
+        values = level2;
+        n_values = used;
+    }
+    return hip_status(launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), s, values, n_values,
+                             extra_sumsq, n_extra, max_norm, flag, norm_out, coef_out),
+                      fn);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for the allocation-free norm (zero_grad_norm_noalloc)
+// ---------------------------------------------------------------------------
+
+// Laid out as a workspace of one set at the largest n: pointer table, second-
+// level sums, then one fp64 partial sum per 2048 elements.
+constexpr int64_t kNoAllocScratchBytes = kPartialsOffset + int64_t(sizeof(double)) * (ZERO_NOALLOC_MAX_ELEMS / kPartialElems);
+static_assert(ZERO_NOALLOC_MAX_ELEMS % kPartialElems == 0, "the largest n fills whole partial ranges");
+static_assert(ZERO_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "the header states the scratch size");
+
+}  // namespace
+}  // namespace zf
+
+// Each GPU the library runs on holds its own copy until the process ends.  In
+// host code this name is a stand-in, not a device address: every use goes
+// through the per-device address from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[zf::kNoAllocScratchBytes];
+
+namespace zf {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, resolved on the first call on
+// that device (with it current) and kept.
+int noalloc_scratch(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZERO_EINVAL, std::string(fn) + ": device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (ptr == nullptr || (addr(ptr) & 255))
+            return fail(ZERO_EHIP, std::string(fn) + ": the scratch array has no usable device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZERO_OK;
+}
+
 }  // namespace
 }  // namespace zf
 
@@ -680,66 +793,21 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
 int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale, void* workspace,
                    int64_t workspace_bytes, int n_sets, const double* extra_sumsq, int n_extra,
                    float max_norm, int32_t* flag, double* norm_out, float* coef_out, void* stream) {
-    const char* fn = "zero_grad_norm";
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
-    if (n_sets < 1 || n_sets > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": n_sets must be in [1, 1024]");
-    if (n_extra < 0 || (n_extra > 0 && (extra_sumsq == nullptr || (addr(extra_sumsq) & 7))))
-        return fail(ZERO_EINVAL, std::string(fn) + ": bad extra_sumsq");
-    if (!std::isfinite(max_norm)) return fail(ZERO_EINVAL, std::string(fn) + ": max_norm must be finite");
-    if (workspace == nullptr || (addr(workspace) & 7))
-        return fail(ZERO_EINVAL, std::string(fn) + ": workspace NULL or not 8-byte aligned");
-    if (workspace_bytes < zero_workspace_bytes(n, n_sets))
-        return fail(ZERO_EINVAL, std::string(fn) + ": workspace too small");
-    if (flag == nullptr || (addr(flag) & 3) || norm_out == nullptr || (addr(norm_out) & 7) ||
-        coef_out == nullptr || (addr(coef_out) & 3))
-        return fail(ZERO_EINVAL, std::string(fn) + ": flag, norm_out or coef_out NULL or misaligned");
-    if (grad != nullptr) {
-        if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
-        if (!pow2_positive(inv_loss_scale))
-            return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
-        if (n > 0 && (addr(grad) & 1)) return fail(ZERO_EINVAL, std::string(fn) + ": grad misaligned");
-        if (overlaps(grad, 2 * n, workspace, workspace_bytes))
-            return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps grad");
-    }
-    if (overlaps(norm_out, 8, workspace, workspace_bytes) || overlaps(coef_out, 4, workspace, workspace_bytes) ||
-        overlaps(flag, 4, workspace, workspace_bytes) || overlaps(norm_out, 8, coef_out, 4))
-        return fail(ZERO_EALIAS, std::string(fn) + ": outputs overlap");
+    return grad_norm_enqueue("zero_grad_norm", grad, n, dtype, inv_loss_scale, workspace, workspace_bytes, n_sets,
+                             extra_sumsq, n_extra, max_norm, flag, norm_out, coef_out, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t blocks = partial_blocks(n);
-    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kPartialsOffset);
-    double* level2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + kTableBytes);
-    if (grad != nullptr && n > 0) {
-        const void* p16[1] = {grad};
-        const Span sp = make_span(n, p16, 1, nullptr, 0);
-        const uint16_t* g16 = static_cast<const uint16_t*>(grad);
-        const dim3 grid{unsigned(ceil_div(blocks, int64_t(kSumsqWaves) * kSumsqRangesPerWave))};
-        const hipError_t e =
-            dtype == ZERO_F16
-                ? launch(sumsq_kernel<ZERO_F16>, grid, dim3(kSumsqBlock), s, g16, sp, inv_loss_scale, blocks,
-                         partials, flag)
-                : launch(sumsq_kernel<ZERO_BF16>, grid, dim3(kSumsqBlock), s, g16, sp, inv_loss_scale, blocks,
-                         partials, flag);
-        if (e != hipSuccess) return hip_status(e, fn);
-    }
-    // With n = 0 every partial sum is zero by definition: none is read, so an
-    // empty gradient needs no partials pass and no earlier launch.
-    const int64_t count = n > 0 ? int64_t(n_sets) * blocks : 0;
-    const double* values = partials;
-    int64_t n_values = count;
-    if (count > kSingleStageMax) {
-        const int64_t groups = std::min<int64_t>(kLevel2Max, ceil_div(count, kStageChunkMin));
-        const int64_t chunk = ceil_div(count, groups);
-        const int64_t used = ceil_div(count, chunk);
-        const hipError_t e = launch(fold_kernel, dim3(unsigned(used)), dim3(kStageBlock), s, partials, count,
-                                    chunk, level2);
-        if (e != hipSuccess) return hip_status(e, fn);
-        values = level2;
-        n_values = used;
-    }
-    return hip_status(launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), s, values, n_values,
-                             extra_sumsq, n_extra, max_norm, flag, norm_out, coef_out),
-                      fn);
+int zero_grad_norm_noalloc(const void* grad, int64_t n, int dtype, float inv_loss_scale,
+                           const double* extra_sumsq, int n_extra, float max_norm, int32_t* flag,
+                           double* norm_out, float* coef_out, void* stream) {
+    const char* fn = "zero_grad_norm_noalloc";
+    if (grad == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": grad is NULL (the partials pass is required)");
+    if (n < 0 || n > ZERO_NOALLOC_MAX_ELEMS)
+        return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, ZERO_NOALLOC_MAX_ELEMS = 2^34]");
+    void* ws = nullptr;
+    if (int rc = noalloc_scratch(fn, &ws)) return rc;
+    return grad_norm_enqueue(fn, grad, n, dtype, inv_loss_scale, ws, kNoAllocScratchBytes, 1, extra_sumsq, n_extra,
+                             max_norm, flag, norm_out, coef_out, stream);
 }
 
 int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
