@@ -54,6 +54,15 @@ namespace {
 // a1: reduce
 // ---------------------------------------------------------------------------
 
+#ifndef ZF_RANK_UNROLL_FULL
+#define ZF_RANK_UNROLL_FULL 8
+#endif
+#ifndef ZF_RANK_UNROLL_WIDE
+#define ZF_RANK_UNROLL_WIDE 4
+#endif
+constexpr int kRankUnrollFull = ZF_RANK_UNROLL_FULL;
+constexpr int kRankUnrollWide = ZF_RANK_UNROLL_WIDE;
+
 // ND > 0: rank count known at compile time (<= 64), pointers in kernel args.
 // ND == 0: runtime rank count <= 64, pointers in kernel args.
 // ND < 0: runtime rank count > 64, pointers in a device table (workspace).
@@ -105,10 +114,12 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(Ptrs64 tab, const 
                     for (int k = 0; k < 4; ++k) acc[u][k] = widen<DT>(half_of(w, k));
                 }
                 if constexpr (ND > 0) {
-                    // Up to 16 ranks unroll fully; beyond, 8 ranks' loads are in
-                    // flight at a time (a full unroll spills registers).  The
-                    // summation order is rank order either way.
-                    constexpr int kRankUnroll = ND > 16 ? 8 : ND;
+                    // Up to kRankUnrollFull ranks unroll fully; beyond, the rank
+                    // loop unrolls by kRankUnrollWide, so that many ranks' loads
+                    // are in flight at a time (a full unroll of 16 or more ranks
+                    // holds them all in registers and halves the waves per SIMD).
+                    // The summation order is rank order either way.
+                    constexpr int kRankUnroll = ND > kRankUnrollFull ? kRankUnrollWide : ND;
 #pragma unroll kRankUnroll
                     for (int r = 1; r < ND; ++r) {
                         u2 w[kReduceQuadsPerLane];
