@@ -375,7 +375,7 @@ def checkpoint_bench(directory, name, seed):
         save_s = []
         for r, path in enumerate(paths):   # the other ranks' files hold this rank's arrays, same sizes
             t0 = time.perf_counter()
-            abi.zero_ckpt_save(path, run.plan, r, run.t - 1, *state, staging)
+            abi.zero_ckpt_save(path, run.plan, r, run.counters()[1], *state, staging)
             save_s.append(time.perf_counter() - t0)
         out = [torch.empty_like(state[0]) for _ in range(3)]
         t0 = time.perf_counter()
@@ -535,8 +535,8 @@ def main():
         ev = {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for p in phases + ["step"]}
         events.append(ev)
+        run._ensure_table()
         ev["step"][0].record(stream)
-        run.flag.zero_()
         if not w.pre_reduced:
             ev["reduce"][0].record(stream)
             run.reduce_all()
@@ -555,8 +555,8 @@ def main():
             ev["gather"][0].record(stream)
             run.gather_all()
             ev["gather"][1].record(stream)
+        run.end_step()
         ev["step"][1].record(stream)
-        run.t += 1
     torch.cuda.synchronize()
     del lead
     per_step = {p: [] for p in phases}
@@ -596,7 +596,7 @@ def main():
     owned = run.n * len(run.owners)
     alg_bytes = run.algorithmic_bytes()
     step_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    flag = int(run.flag.item())
+    t_next, applied, skipped, flag = run.counters()
     # The dominant kernel: the phase with the longest time per step.  Its
     # launches are timed together, so the per-launch time is the phase time
     # over its launch count (gaps between launches included).
@@ -674,6 +674,8 @@ def main():
             "launches_per_step": phase_model[dom]["launches"],
         },
         "step_flag": flag,
+        "steps_applied": applied,
+        "steps_skipped": skipped,
         "norm": float(run.norm.item()),
         "clip_coef": float(run.coef.item()),
     }

@@ -78,6 +78,7 @@ extern "C" {
 /* Bits of the int32 step flag (device memory, OR-ed by the kernels). */
 #define ZERO_FLAG_NONFINITE_GRAD 1 /* an input or reduced gradient is inf/NaN */
 #define ZERO_FLAG_NONFINITE_NORM 2 /* the sum of squares is not finite */
+#define ZERO_FLAG_NO_CONSTS 4      /* zero_adam_step_owners: no table entry for the step */
 
 /* ---------------------------------------------------------------------- */
 /* a0: partition (host only, integer arithmetic)                           */
@@ -212,6 +213,27 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
                       float inv_loss_scale, void* reduced_out, void* workspace,
                       int64_t workspace_bytes, int set, int32_t* flag, void* stream);
 
+/*
+ * zero_reduce_owners -- zero_reduce_shard for `owners` emulated owners in one
+ * launch, as when every rank of a data-parallel group is emulated on one GPU
+ * (L18 notes §2.5, the 4-card simulation; the reduce-scatter's local half for
+ * each owner, §2.2 step 3).  Owner o's contribution from rank r starts
+ * o * contrib_stride elements past contribs[r]; its output starts
+ * o * reduced_stride elements past reduced_out; its partial sums go to
+ * workspace set o.  The result equals `owners` calls of zero_reduce_shard
+ * with set = o, bit for bit.
+ *
+ * 1 <= owners <= 1024; with owners > 1, 0 <= contrib_stride <= 2^40 and
+ * n <= reduced_stride <= 2^40 (owners' outputs do not overlap).  Strides
+ * that are multiples of 4 keep the vector path.  workspace_bytes >=
+ * zero_workspace_bytes(n, owners).  Other arguments and errors as
+ * zero_reduce_shard.
+ */
+int zero_reduce_owners(const void* const* contribs, int nd, int64_t n, int owners,
+                       int64_t contrib_stride, int dtype, float inv_loss_scale, void* reduced_out,
+                       int64_t reduced_stride, void* workspace, int64_t workspace_bytes,
+                       int32_t* flag, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* a2: global gradient norm and clip coefficient                           */
 /* ---------------------------------------------------------------------- */
@@ -337,6 +359,54 @@ int zero_adam_consts_fill(const zero_adam_hparams* hp, zero_adam_consts* out);
 int zero_adam_step_consts(float* master, float* m, float* v, const void* grad, int grad_dtype,
                           int64_t n, const zero_adam_consts* consts_dev, const float* coef_dev,
                           const int32_t* flag, void* param_out, int param_dtype, void* stream);
+
+/*
+ * The device side of a step sequence: the step count t of the next update,
+ * kept in device memory so that steps (and captured graph replays) need no
+ * host round trip, and advanced only by applied steps -- a step skipped for
+ * a non-finite gradient leaves t, and so the bias corrections, unchanged.
+ * Initialise it on the device as {step = first t (>= 1), 0, 0, table_t0, 0, 0}.
+ */
+typedef struct {
+    int64_t step;       /* t of the next update, >= 1 */
+    int64_t applied;    /* steps applied */
+    int64_t skipped;    /* steps skipped (a set flag) */
+    int64_t table_t0;   /* the step of entry 0 of the scalars table */
+    int32_t last_flag;  /* the flag of the last step that ended */
+    int32_t reserved;
+} zero_step_state;
+
+/*
+ * zero_adam_step_owners -- zero_adam_step for `owners` emulated owners in one
+ * launch (L18 notes §2.5; each owner updates its own slice, §2.2 step 4),
+ * with the step's scalars chosen on the device: entry
+ * state_dev->step - state_dev->table_t0 of table_dev, a device array of
+ * table_len zero_adam_consts (from zero_adam_consts_fill for consecutive
+ * steps).  If that index is outside the table, or *flag != 0, nothing is
+ * written; the former also sets ZERO_FLAG_NO_CONSTS in *flag.  Owner o's
+ * master, m and v start o * state_stride elements past master, m and v, its
+ * gradient o * grad_stride past grad, its 16-bit output o * param_stride
+ * past param_out.  The same kernel and bits as zero_adam_step.
+ *
+ * 1 <= owners <= 1024; with owners > 1, n <= state_stride, param_stride <=
+ * 2^40 and 0 <= grad_stride <= 2^40.  1 <= table_len <= 2^31.  state_dev:
+ * device, 8-byte aligned.  flag: device int32 (written only as above).
+ * Other arguments and errors as zero_adam_step.
+ */
+int zero_adam_step_owners(float* master, float* m, float* v, int64_t state_stride,
+                          const void* grad, int grad_dtype, int64_t grad_stride, int64_t n,
+                          int owners, const zero_adam_consts* table_dev, int64_t table_len,
+                          const zero_step_state* state_dev, const float* coef_dev, int32_t* flag,
+                          void* param_out, int64_t param_stride, int param_dtype, void* stream);
+
+/*
+ * zero_step_end -- closes a step on the device (one thread): records *flag in
+ * state_dev->last_flag; if it is 0 the step was applied and step and applied
+ * advance by one, otherwise skipped does; then *flag is cleared for the next
+ * step.  Enqueue it after the step's last AdamW call.  Errors: ZERO_EINVAL
+ * (NULL or misaligned), ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_step_end(int32_t* flag, zero_step_state* state_dev, void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* a4: gather of 16-bit shards into the full parameter buffer              */

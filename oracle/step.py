@@ -247,6 +247,28 @@ def step_sharded(plan, local_grads, states, hp, step, grad_dtype, param_dtype):
     return result
 
 
+def step_sequence(plan, grads_per_step, states, hp, grad_dtype, param_dtype, first_step=1):
+    """Consecutive sharded steps; the step count advances only for applied steps.
+
+    ``grads_per_step[k]`` is the list of every rank's full local gradient for
+    step k.  A step with a non-finite gradient is skipped whole: the state
+    and the step count stay as they were, so the next update takes the bias
+    corrections the skipped one would have taken (the pages give no overflow
+    policy; a skipped step is treated as if it had not happened).  Returns
+    one step_sharded result per step, each with the step count ``t`` it used.
+    """
+    t = first_step
+    out = []
+    for grads in grads_per_step:
+        res = step_sharded(plan, grads, states, hp, t, grad_dtype, param_dtype)
+        res["t"] = t
+        out.append(res)
+        if not res["skipped"]:
+            states = res["states"]
+            t += 1
+    return out
+
+
 def step_unsharded(local_grads, master, m, v, hp, step, grad_dtype, param_dtype):
     """Plain data parallelism: every rank reduces and updates the whole vector.
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert abi.zero_version() == 10100
+    assert abi.zero_version() == 10200
 
 
 @pytest.mark.parametrize("seed", range(60))
@@ -179,6 +179,66 @@ def test_adam_rejects(bad, code):
 
 def test_adam_zero_length_is_a_no_op():
     _adam(n=0, master=None, m=None, v=None, grad=None, param_out=None)
+
+
+def _reduce_owners(**kw):
+    args = dict(contribs=[A, A + 16384], n=1024, owners=3, contrib_stride=2048, dtype=abi.ZERO_F16,
+                inv_loss_scale=1.0, reduced_out=B, reduced_stride=1024, workspace=W, flag=F, stream=0,
+                workspace_bytes=abi.zero_workspace_bytes(1024, 3))
+    args.update(kw)
+    return abi.zero_reduce_owners(**args)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(owners=0), abi.ZERO_EINVAL),
+    (dict(owners=1025), abi.ZERO_EINVAL),
+    (dict(reduced_stride=1023), abi.ZERO_EINVAL),            # owners' outputs would overlap
+    (dict(contrib_stride=-1), abi.ZERO_EINVAL),
+    (dict(contrib_stride=(1 << 40) + 1), abi.ZERO_EINVAL),
+    (dict(workspace_bytes=abi.zero_workspace_bytes(1024, 2)), abi.ZERO_EINVAL),   # room for 2 sets of 3
+    (dict(reduced_out=A + 2 * 4096), abi.ZERO_EALIAS),        # inside rank 0's third owner's contribution
+    (dict(workspace=B + 2 * 2048), abi.ZERO_EALIAS),           # inside the last owner's output
+])
+def test_reduce_owners_rejects(bad, code):
+    with pytest.raises(abi.ZeroError) as e:
+        _reduce_owners(**bad)
+    assert e.value.code == code
+
+
+def _adam_owners(**kw):
+    n = 1024
+    args = dict(master=A, m=A + 4 * 4 * n, v=A + 8 * 4 * n, state_stride=n, grad=B, grad_dtype="bf16",
+                grad_stride=n, n=n, owners=4, table_dev=W, table_len=8, state_dev=W + 4096, coef=F, flag=F + 4,
+                param_out=B + 2 * 4 * n, param_stride=n, param_dtype="bf16", stream=0)
+    args.update(kw)
+    return abi.zero_adam_step_owners(**args)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(owners=0), abi.ZERO_EINVAL),
+    (dict(state_stride=1000), abi.ZERO_EINVAL),
+    (dict(param_stride=1000), abi.ZERO_EINVAL),
+    (dict(grad_stride=-4), abi.ZERO_EINVAL),
+    (dict(table_len=0), abi.ZERO_EINVAL),
+    (dict(table_dev=0), abi.ZERO_EINVAL),
+    (dict(state_dev=W + 4100), abi.ZERO_EINVAL),              # not 8-byte aligned
+    (dict(m=A + 3 * 4 * 1024), abi.ZERO_EALIAS),              # overlaps the last owner's master
+    (dict(param_out=B + 2 * 3 * 1024), abi.ZERO_EALIAS),      # overlaps the last owner's gradient
+    (dict(table_dev=A + 64), abi.ZERO_EALIAS),
+    (dict(state_dev=A + 4 * 4096), abi.ZERO_EALIAS),
+])
+def test_adam_owners_rejects(bad, code):
+    with pytest.raises(abi.ZeroError) as e:
+        _adam_owners(**bad)
+    assert e.value.code == code
+
+
+def test_step_end_rejects():
+    for flag, state, code in ((0, W, abi.ZERO_EINVAL), (F + 2, W, abi.ZERO_EINVAL), (F, W + 4, abi.ZERO_EINVAL),
+                              (W + 16, W, abi.ZERO_EALIAS)):
+        with pytest.raises(abi.ZeroError) as e:
+            abi.zero_step_end(flag, state, 0)
+        assert e.value.code == code
 
 
 def test_grad_norm_rejects():

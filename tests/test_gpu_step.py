@@ -74,6 +74,42 @@ def test_tiny_all_ranks_three_steps(runner):
         states = ref["states"]
 
 
+def test_tiny_skipped_step_keeps_the_step_count(runner):
+    # Step 2 of 3 carries an inf in one rank's gradient: it is skipped whole
+    # (state and parameters unchanged), and step 3 takes t = 2, as the oracle's
+    # step sequence does; the device counters say so.
+    w = workloads.get("tiny_nd4_z2")
+    _note("tiny workload: a skipped step in the middle")
+    run = runner.RankStep(w, seed=12)
+    plan = partition.make_plan(w.units, w.nd, w.stage, w.align)
+    states = [(_np32(run.master[i]), _np32(run.m[i]), _np32(run.v[i])) for i in range(w.nd)]
+    grads, snaps = [], []
+    for k in range(3):
+        if k > 0:
+            run.fresh_gradients(step=k)
+        if k == 1:
+            run.local[2, 12_345] = float("inf")
+        grads.append([synth.bits(run.local[r, :w.psi]) for r in range(w.nd)])
+        run.step()
+        torch.cuda.synchronize()
+        snaps.append(([(_np32(run.master[i]), _np32(run.m[i]), _np32(run.v[i])) for i in range(w.nd)],
+                      synth.bits(run.full), run.counters()))
+    ref = step.step_sequence(plan, grads, states, _hp(w), w.grad_dtype, w.param_dtype)
+    assert [r["t"] for r in ref] == [1, 2, 2] and [r["skipped"] for r in ref] == [False, True, False]
+    assert snaps[0][2][:3] == (2, 1, 0) and snaps[1][2][:3] == (2, 1, 1) and snaps[2][2][:3] == (3, 2, 1)
+    assert snaps[1][2][3] & 1 and snaps[2][2][3] == 0           # the last flag of each step
+    n = plan.shard_numel
+    for k in (0, 2):
+        for i in range(w.nd):
+            got = snaps[k][0][i] + (snaps[k][1][i * n:(i + 1) * n],)
+            expect = tuple(ref[k]["states"][i]) + (ref[k]["full"][i * n:(i + 1) * n],)
+            adam_parity(got, expect, w.param_dtype, f"step {k + 1} owner {i}")
+    for i in range(w.nd):                                         # the skipped step changed nothing
+        for a, b in zip(snaps[1][0][i], snaps[0][0][i]):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(snaps[1][1], snaps[0][1])
+
+
 def _single_rank_reference(run, w, state, t):
     """Oracle result for the run's one emulated owner at step t from the oracle's own state."""
     hp = _hp(w)

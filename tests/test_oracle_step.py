@@ -362,6 +362,30 @@ def test_non_finite_skips_the_whole_step():
             assert got is ref
 
 
+def test_skipped_step_is_as_if_it_never_happened():
+    # Three steps with a NaN in the second: the third update equals the second
+    # of a run without the bad step (same state, same step count t = 2), and
+    # differs from an update that took t = 3 (the bias corrections matter).
+    psi, nd = 2048, 4
+    plan = partition.make_plan([psi], nd, 2)
+    rng = np.random.default_rng(18)
+    grads = [[_rand16(rng, psi, 1e-3, F16) for _ in range(nd)] for _ in range(3)]
+    grads[1][2] = grads[1][2].copy()
+    grads[1][2][77] = 0x7C00        # +inf in one rank's gradient of step 2
+    _, master, m, v = _setup(psi, nd, seed=19)
+    states = [tuple(partition.shard_of(plan, a, r) for a in (master, m, v)) for r in range(nd)]
+    hp = AdamHparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_norm=1.0)
+    run = step.step_sequence(plan, grads, states, hp, F16, F16)
+    assert [r["t"] for r in run] == [1, 2, 2] and [r["skipped"] for r in run] == [False, True, False]
+    clean = step.step_sequence(plan, [grads[0], grads[2]], states, hp, F16, F16)
+    assert np.array_equal(run[2]["full"], clean[1]["full"])
+    for a, b in zip(run[2]["states"], clean[1]["states"]):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    advanced = step.step_sharded(plan, grads[2], run[0]["states"], hp, 3, F16, F16)
+    assert not np.array_equal(advanced["full"], run[2]["full"])
+
+
 def test_padding_stays_zero():
     # Padded positions carry zero gradient and zero state; Adam keeps them 0.
     units, nd = [1000], 16       # slice 64, 1024 padded, 24 padding elements

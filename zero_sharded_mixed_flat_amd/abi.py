@@ -30,6 +30,7 @@ ZERO_MAX_RANKS = 1024
 ZERO_MAX_ELEMS = 1 << 34
 ZERO_FLAG_NONFINITE_GRAD = 1
 ZERO_FLAG_NONFINITE_NORM = 2
+ZERO_FLAG_NO_CONSTS = 4
 
 # Every symbol include/zero_flat.h declares.
 EXPORTED = (
@@ -40,7 +41,7 @@ EXPORTED = (
     "zero_quant_code_bytes", "zero_quant_scale_count", "zero_quantize_blocks", "zero_dequantize_blocks",
     "zero_gather_dequant", "zero_cpu_adam_step", "zero_offload_adam_step", "zero_cpu_isa", "zero_cpu_set_isa",
     "zero_plan_reshard", "zero_ckpt_save", "zero_ckpt_load", "zero_adam_consts_fill", "zero_adam_step_consts",
-    "zero_grad_norm_noalloc",
+    "zero_grad_norm_noalloc", "zero_reduce_owners", "zero_adam_step_owners", "zero_step_end",
 )
 ZERO_QBLOCK = 256
 ZERO_CPU_SCALAR = 0
@@ -77,6 +78,11 @@ class zero_adam_hparams(ctypes.Structure):
                 ("inv_loss_scale", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
+class zero_step_state(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("applied", ctypes.c_int64), ("skipped", ctypes.c_int64),
+                ("table_t0", ctypes.c_int64), ("last_flag", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class zero_adam_consts(ctypes.Structure):
     _fields_ = [(name, ctypes.c_float) for name in (
         "lr", "beta1", "beta2", "one_minus_beta1", "one_minus_beta2", "eps", "weight_decay", "inv_loss_scale",
@@ -110,6 +116,11 @@ _sig = {
     "zero_grad_norm": (_I, [_P, _I64, _I, ctypes.c_float, _P, _I64, _I, _P, _I, ctypes.c_float, _P, _P,
                             _P, _P]),
     "zero_grad_norm_noalloc": (_I, [_P, _I64, _I, ctypes.c_float, _P, _I, ctypes.c_float, _P, _P, _P, _P]),
+    "zero_reduce_owners": (_I, [ctypes.POINTER(_P), _I, _I64, _I, _I64, _I, ctypes.c_float, _P, _I64, _P, _I64,
+                                _P, _P]),
+    "zero_adam_step_owners": (_I, [_P, _P, _P, _I64, _P, _I, _I64, _I64, _I, _P, _I64, _P, _P, _P, _P, _I64, _I,
+                                   _P]),
+    "zero_step_end": (_I, [_P, _P, _P]),
     "zero_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
                             _P]),
     "zero_gather_params": (_I, [_P, ctypes.POINTER(_P), _I, _I, _I, _P, _P, _I64, _P]),
@@ -359,6 +370,46 @@ def zero_reduce_shard(contribs, n, dtype, inv_loss_scale, reduced_out, workspace
     _check(lib.zero_reduce_shard(ptrs, len(contribs), int(n), _dtype(dtype), float(inv_loss_scale),
                                  _ptr(reduced_out), _ptr(workspace), wb, int(set_index), _ptr(flag),
                                  _stream(stream)))
+
+
+def zero_reduce_owners(contribs, n, owners, contrib_stride, dtype, inv_loss_scale, reduced_out, reduced_stride,
+                       workspace, flag, stream=None, workspace_bytes=None):
+    """``contribs``: one device tensor (or a PointerTable) per rank, each holding every owner's
+    contribution from that rank (owner o's at element o * contrib_stride)."""
+    span = (owners - 1) * contrib_stride + n if n > 0 else 0
+    ptrs = _table(contribs, 2 * span, "contribution")
+    _need(reduced_out, 2 * ((owners - 1) * reduced_stride + n) if n > 0 else 0, "reduced_out")
+    _need(flag, 4, "flag")
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(lib.zero_reduce_owners(ptrs, len(contribs), int(n), int(owners), int(contrib_stride), _dtype(dtype),
+                                  float(inv_loss_scale), _ptr(reduced_out), int(reduced_stride), _ptr(workspace), wb,
+                                  _ptr(flag), _stream(stream)))
+
+
+def step_state(first_step=1, table_t0=1):
+    """A zero_step_state for the device (copy it into 40 device bytes)."""
+    return zero_step_state(int(first_step), 0, 0, int(table_t0), 0, 0)
+
+
+def zero_adam_step_owners(master, m, v, state_stride, grad, grad_dtype, grad_stride, n, owners, table_dev,
+                          table_len, state_dev, coef, flag, param_out, param_stride, param_dtype, stream=None):
+    ext = lambda stride, b: b * ((owners - 1) * stride + n) if n > 0 else 0
+    for t, b, what in ((master, ext(state_stride, 4), "master"), (m, ext(state_stride, 4), "m"),
+                       (v, ext(state_stride, 4), "v"), (grad, ext(grad_stride, 2), "grad"),
+                       (param_out, ext(param_stride, 2), "param_out"), (coef, 4, "coef"), (flag, 4, "flag"),
+                       (table_dev, table_len * ctypes.sizeof(zero_adam_consts), "table_dev"),
+                       (state_dev, ctypes.sizeof(zero_step_state), "state_dev")):
+        _need(t, b, what)
+    _check(lib.zero_adam_step_owners(_ptr(master), _ptr(m), _ptr(v), int(state_stride), _ptr(grad),
+                                     _dtype(grad_dtype), int(grad_stride), int(n), int(owners), _ptr(table_dev),
+                                     int(table_len), _ptr(state_dev), _ptr(coef), _ptr(flag), _ptr(param_out),
+                                     int(param_stride), _dtype(param_dtype), _stream(stream)))
+
+
+def zero_step_end(flag, state_dev, stream=None):
+    _need(flag, 4, "flag")
+    _need(state_dev, ctypes.sizeof(zero_step_state), "state_dev")
+    _check(lib.zero_step_end(_ptr(flag), _ptr(state_dev), _stream(stream)))
 
 
 def zero_grad_norm(grad, n, dtype, inv_loss_scale, workspace, n_sets, extra_sumsq, n_extra, max_norm,

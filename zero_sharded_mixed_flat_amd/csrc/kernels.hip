@@ -63,26 +63,38 @@ namespace {
 constexpr int kRankUnrollFull = ZF_RANK_UNROLL_FULL;
 constexpr int kRankUnrollWide = ZF_RANK_UNROLL_WIDE;
 
+// Element offsets of emulated owner o's slices (blockIdx.y = o): its
+// contribution from rank r starts `contrib` elements past owner 0's, its output
+// `out` past, its partial sums `partials` sums past.  All zero for one owner.
+struct OwnerStrides {
+    int64_t contrib, out, partials;
+};
+
 // ND > 0: rank count known at compile time (<= 64), pointers in kernel args.
 // ND == 0: runtime rank count <= 64, pointers in kernel args.
 // ND < 0: runtime rank count > 64, pointers in a device table (workspace).
-// Block b covers quads [b*kPartialQuads, (b+1)*kPartialQuads) of the body (or
-// elements [b*kPartialElems, ...) without `vec`) and writes partials[b].
+// Block (b, o) covers quads [b*kPartialQuads, (b+1)*kPartialQuads) of owner
+// o's body (or elements [b*kPartialElems, ...) without `vec`) and writes
+// owner o's partials[b].
 template <int DT, int ND>
 __global__ __launch_bounds__(kReduceBlock) void reduce_kernel(Ptrs64 tab, const uint16_t* const* dtab,
-                                                        int nd, Span sp, float inv_nd, float nd_f,
-                                                        int pow2, float inv_s,
+                                                        int nd, Span sp, OwnerStrides os, float inv_nd,
+                                                        float nd_f, int pow2, float inv_s,
                                                         uint16_t* __restrict__ out,
                                                         double* __restrict__ partials,
                                                         int32_t* __restrict__ flag) {
 #pragma clang fp contract(off)
     const int ranks = ND > 0 ? ND : nd;
+    const int64_t owner = blockIdx.y;
+    const int64_t coff = owner * os.contrib;
+    out += owner * os.out;
+    partials += owner * os.partials;
     double sq = 0.0;
     int bad = 0;
 
     auto src = [&](int r) -> const uint16_t* {
-        if constexpr (ND >= 0) return tab.p[r];
-        else return dtab[r];
+        if constexpr (ND >= 0) return tab.p[r] + coff;
+        else return dtab[r] + coff;
     };
     auto finish = [&](float acc) -> uint32_t {
         const float mean = pow2 ? acc * inv_nd : acc / nd_f;
@@ -324,10 +336,20 @@ struct AdamConsts {
     float lr, b1, b2, omb1, omb2, eps, wd, inv_s, bc1, bc2;
 };
 
-// Block b covers quads [b*kAdamTileQuads, (b+1)*kAdamTileQuads) of the body (or
-// elements [b*kAdamTileElems, ...) without `vec`).
-// DEV: the scalars come from device memory (c_dev) instead of the kernel
-// arguments, so a captured graph can replay the launch with new ones.
+// Where an AdamW launch takes its scalars from.
+enum ConstsFrom { kConstsArg = 0, kConstsDevice = 1, kConstsTable = 2 };
+
+// Element offsets of emulated owner o's arrays (blockIdx.y = o).
+struct AdamStrides {
+    int64_t state, grad, param;
+};
+
+// Block (b, o) covers quads [b*kAdamTileQuads, (b+1)*kAdamTileQuads) of owner
+// o's body (or elements [b*kAdamTileElems, ...) without `vec`).
+// CF selects the scalars: the kernel argument c_arg; *c_src, so a captured
+// graph can replay the launch with new ones; or c_src[state->step -
+// state->table_t0], a table entry per step chosen by the device step counter
+// (an entry outside the table skips the step and sets ZERO_FLAG_NO_CONSTS).
 // The update widens the fp32 state, the 16-bit gradient and the fp32 scalars
 // to fp64 and evaluates it there one operation at a time, in the order
 // written, with no fused multiply-adds and with correctly rounded division
@@ -335,18 +357,39 @@ struct AdamConsts {
 // unsharded update's own definition, so every output is the one the plain
 // data-parallel step gives (L18 notes §2.5), and the host AdamW, which
 // evaluates the same sequence, gives the same bits.
-template <int GDT, int PDT, bool DEV>
+template <int GDT, int PDT, int CF>
 __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ master,
                                                       float* __restrict__ m,
                                                       float* __restrict__ v,
                                                       const uint16_t* __restrict__ grad, Span sp,
-                                                      AdamConsts c_arg, const AdamConsts* __restrict__ c_dev,
+                                                      AdamStrides as, AdamConsts c_arg,
+                                                      const AdamConsts* __restrict__ c_src, int64_t table_len,
+                                                      const zero_step_state* __restrict__ state,
                                                       const float* __restrict__ coef_dev,
-                                                      const int32_t* __restrict__ flag,
+                                                      int32_t* __restrict__ flag,
                                                       uint16_t* __restrict__ param) {
 #pragma clang fp contract(off)
     if (*flag != 0) return;  // a skipped step writes nothing
-    const AdamConsts c = DEV ? *c_dev : c_arg;
+    AdamConsts c = c_arg;
+    if constexpr (CF == kConstsDevice) {
+        c = *c_src;
+    } else if constexpr (CF == kConstsTable) {
+        // Every block takes the same decision from the same inputs.
+        const int64_t idx = state->step - state->table_t0;
+        if (idx < 0 || idx >= table_len) {
+            if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(flag, ZERO_FLAG_NO_CONSTS);
+            return;
+        }
+        c = c_src[idx];
+    }
+    {
+        const int64_t owner = blockIdx.y;
+        master += owner * as.state;
+        m += owner * as.state;
+        v += owner * as.state;
+        grad += owner * as.grad;
+        param += owner * as.param;
+    }
     // inv_s is a power of two, so this product is exact and g below is the
     // 16-bit value times inv_s times coef with a single rounding.
     const double gs = double(c.inv_s) * double(*coef_dev);
@@ -435,6 +478,23 @@ __global__ __launch_bounds__(kAdamBlock) void adam_kernel(float* __restrict__ ma
     }
 }
 
+// One thread closes a step: an applied step (flag 0) advances the device step
+// counter; a skipped one is counted; the flag is recorded and cleared for the
+// next step.
+__global__ __launch_bounds__(64) void step_end_kernel(int32_t* __restrict__ flag,
+                                                      zero_step_state* __restrict__ st) {
+    if (threadIdx.x != 0) return;
+    const int32_t f = *flag;
+    st->last_flag = f;
+    if (f == 0) {
+        st->step += 1;
+        st->applied += 1;
+    } else {
+        st->skipped += 1;
+    }
+    *flag = 0;
+}
+
 // ---------------------------------------------------------------------------
 // a4: gather one unit
 // ---------------------------------------------------------------------------
@@ -503,10 +563,10 @@ __global__ __launch_bounds__(kGatherBlock) void gather_kernel(Ptrs64 tab, const 
 
 template <int DT>
 hipError_t launch_reduce(int nd, dim3 grid, hipStream_t s, const Ptrs64& tab,
-                         const uint16_t* const* dtab, Span sp, float inv_nd, float nd_f, int pow2,
-                         float inv_s, uint16_t* out, double* partials, int32_t* flag) {
-#define ZF_REDUCE(ND_)                                                                             \
-    return launch(reduce_kernel<DT, ND_>, grid, dim3(kReduceBlock), s, tab, dtab, nd, sp, inv_nd, nd_f, \
+                         const uint16_t* const* dtab, Span sp, const OwnerStrides& os, float inv_nd, float nd_f,
+                         int pow2, float inv_s, uint16_t* out, double* partials, int32_t* flag) {
+#define ZF_REDUCE(ND_)                                                                                  \
+    return launch(reduce_kernel<DT, ND_>, grid, dim3(kReduceBlock), s, tab, dtab, nd, sp, os, inv_nd, nd_f, \
                   pow2, inv_s, out, partials, flag)
     switch (dtab ? -1 : nd) {
         case -1: ZF_REDUCE(-1);
@@ -522,24 +582,47 @@ hipError_t launch_reduce(int nd, dim3 grid, hipStream_t s, const Ptrs64& tab,
 #undef ZF_REDUCE
 }
 
-template <int GDT, int PDT>
-hipError_t launch_adam_p(const AdamConsts* c_dev, dim3 grid, hipStream_t s, float* master, float* m, float* v,
-                         const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
-                         const int32_t* flag, uint16_t* param) {
-    if (c_dev != nullptr)
-        return launch(adam_kernel<GDT, PDT, true>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c, c_dev,
-                      coef, flag, param);
-    return launch(adam_kernel<GDT, PDT, false>, grid, dim3(kAdamBlock), s, master, m, v, grad, sp, c,
-                  static_cast<const AdamConsts*>(nullptr), coef, flag, param);
+// The scalars of one AdamW launch: by value, from device memory, or from a
+// per-step table chosen by the device step counter.
+struct AdamSource {
+    int from;
+    AdamConsts arg;
+    const AdamConsts* src;
+    int64_t table_len;
+    const zero_step_state* state;
+};
+
+struct AdamArgs {
+    float* master;
+    float* m;
+    float* v;
+    const uint16_t* grad;
+    uint16_t* param;
+    AdamStrides strides;
+    const float* coef;
+    int32_t* flag;
+};
+
+template <int GDT, int PDT, int CF>
+hipError_t launch_adam_c(dim3 grid, hipStream_t s, Span sp, const AdamArgs& a, const AdamSource& src) {
+    return launch(adam_kernel<GDT, PDT, CF>, grid, dim3(kAdamBlock), s, a.master, a.m, a.v, a.grad, sp, a.strides,
+                  src.arg, src.src, src.table_len, src.state, a.coef, a.flag, a.param);
 }
 
-template <int GDT>
-hipError_t launch_adam(int pdt, const AdamConsts* c_dev, dim3 grid, hipStream_t s, float* master, float* m,
-                       float* v, const uint16_t* grad, Span sp, const AdamConsts& c, const float* coef,
-                       const int32_t* flag, uint16_t* param) {
-    if (pdt == ZERO_F16)
-        return launch_adam_p<GDT, ZERO_F16>(c_dev, grid, s, master, m, v, grad, sp, c, coef, flag, param);
-    return launch_adam_p<GDT, ZERO_BF16>(c_dev, grid, s, master, m, v, grad, sp, c, coef, flag, param);
+template <int GDT, int PDT>
+hipError_t launch_adam_p(dim3 grid, hipStream_t s, Span sp, const AdamArgs& a, const AdamSource& src) {
+    if (src.from == kConstsTable) return launch_adam_c<GDT, PDT, kConstsTable>(grid, s, sp, a, src);
+    if (src.from == kConstsDevice) return launch_adam_c<GDT, PDT, kConstsDevice>(grid, s, sp, a, src);
+    return launch_adam_c<GDT, PDT, kConstsArg>(grid, s, sp, a, src);
+}
+
+hipError_t launch_adam(int gdt, int pdt, dim3 grid, hipStream_t s, Span sp, const AdamArgs& a,
+                       const AdamSource& src) {
+    if (gdt == ZERO_F16)
+        return pdt == ZERO_F16 ? launch_adam_p<ZERO_F16, ZERO_F16>(grid, s, sp, a, src)
+                               : launch_adam_p<ZERO_F16, ZERO_BF16>(grid, s, sp, a, src);
+    return pdt == ZERO_F16 ? launch_adam_p<ZERO_BF16, ZERO_F16>(grid, s, sp, a, src)
+                           : launch_adam_p<ZERO_BF16, ZERO_BF16>(grid, s, sp, a, src);
 }
 
 static_assert(sizeof(zero_adam_consts) == sizeof(AdamConsts), "zero_adam_consts mirrors AdamConsts");
@@ -568,16 +651,41 @@ int adam_consts(const char* fn, const zero_adam_hparams* hp, AdamConsts* c) {
     return ZERO_OK;
 }
 
-// Checks the buffers of an AdamW launch and enqueues it (scalars by value,
-// or from c_dev when it is not NULL).
-int adam_enqueue(const char* fn, float* master, float* m, float* v, const void* grad, int grad_dtype, int64_t n,
-                 const AdamConsts& c, const AdamConsts* c_dev, const float* coef_dev, const int32_t* flag,
-                 void* param_out, int param_dtype, void* stream) {
+// Owner strides are bounded so that every extent below fits in int64.
+constexpr int64_t kMaxOwnerStride = int64_t(1) << 40;
+
+// Owner o's slices of an array sit o * stride elements past owner 0's.  With
+// several owners the vector path needs every stride to keep each owner's
+// alignment (a multiple of 4 elements); otherwise every element goes one by one.
+inline Span owners_span(Span sp, int owners, const int64_t* strides, int n_strides) {
+    if (owners > 1)
+        for (int i = 0; i < n_strides; ++i)
+            if (strides[i] % 4 != 0) return Span{sp.n, 0, 0, 0};
+    return sp;
+}
+
+// Bytes from owner 0's first element to the last owner's last one.
+inline int64_t owners_extent(int owners, int64_t stride, int64_t n, int64_t elem) {
+    return elem * (int64_t(owners - 1) * stride + n);
+}
+
+// Checks the buffers of an AdamW launch over `owners` emulated owners and
+// enqueues it with the scalars `src` names.
+int adam_enqueue(const char* fn, float* master, float* m, float* v, int64_t state_stride, const void* grad,
+                 int grad_dtype, int64_t grad_stride, int64_t n, int owners, void* param_out, int64_t param_stride,
+                 int param_dtype, const AdamSource& src, const float* coef_dev, const int32_t* flag, void* stream) {
     if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
+    if (owners < 1 || owners > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": owners must be in [1, 1024]");
+    if (owners > 1 && (state_stride < n || param_stride < n || grad_stride < 0 || state_stride > kMaxOwnerStride ||
+                       param_stride > kMaxOwnerStride || grad_stride > kMaxOwnerStride))
+        return fail(ZERO_EINVAL, std::string(fn) + ": owner strides must be in [n, 2^40] (state, param) and "
+                                                   "[0, 2^40] (grad)");
     if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
         return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
     if (coef_dev == nullptr || (addr(coef_dev) & 3) || flag == nullptr || (addr(flag) & 3))
         return fail(ZERO_EINVAL, std::string(fn) + ": coef_dev or flag NULL or misaligned");
+    const int64_t src_bytes = src.from == kConstsTable ? src.table_len * int64_t(sizeof(AdamConsts))
+                                                       : src.from == kConstsDevice ? int64_t(sizeof(AdamConsts)) : 0;
     if (n > 0) {
         if (!master || !m || !v || !grad || !param_out)
             return fail(ZERO_EINVAL, std::string(fn) + ": NULL buffer");
@@ -585,31 +693,111 @@ int adam_enqueue(const char* fn, float* master, float* m, float* v, const void* 
             return fail(ZERO_EINVAL, std::string(fn) + ": fp32 buffers must be 4-byte aligned");
         if ((addr(grad) | addr(param_out)) & 1)
             return fail(ZERO_EINVAL, std::string(fn) + ": 16-bit buffers must be 2-byte aligned");
+        const int64_t sb = owners_extent(owners, state_stride, n, 4), pb = owners_extent(owners, param_stride, n, 2);
+        const int64_t gb = owners_extent(owners, grad_stride, n, 2);
         const void* outs[4] = {master, m, v, param_out};
-        const int64_t ob[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+        const int64_t ob[4] = {sb, sb, sb, pb};
         for (int i = 0; i < 4; ++i) {
             for (int j = i + 1; j < 4; ++j)
                 if (overlaps(outs[i], ob[i], outs[j], ob[j]))
                     return fail(ZERO_EALIAS, std::string(fn) + ": master, m, v and param_out must not overlap");
-            if (overlaps(outs[i], ob[i], grad, 2 * n) || overlaps(outs[i], ob[i], coef_dev, 4) ||
-                overlaps(outs[i], ob[i], flag, 4) ||
-                (c_dev != nullptr && overlaps(outs[i], ob[i], c_dev, int64_t(sizeof(AdamConsts)))))
+            if (overlaps(outs[i], ob[i], grad, gb) || overlaps(outs[i], ob[i], coef_dev, 4) ||
+                overlaps(outs[i], ob[i], flag, 4) || overlaps(outs[i], ob[i], src.src, src_bytes) ||
+                (src.state != nullptr && overlaps(outs[i], ob[i], src.state, int64_t(sizeof(zero_step_state)))))
                 return fail(ZERO_EALIAS, std::string(fn) + ": an output overlaps grad, coef, flag or the scalars");
         }
     }
     if (n == 0) return ok();
     const void* p16[2] = {grad, param_out};
     const void* p32[3] = {master, m, v};
-    const Span sp = make_span(n, p16, 2, p32, 3);
+    const int64_t strides[3] = {state_stride, grad_stride, param_stride};
+    const Span sp = owners_span(make_span(n, p16, 2, p32, 3), owners, strides, 3);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t blocks = sp.vec ? std::max<int64_t>(1, ceil_div(sp.nq, kAdamTileQuads)) : ceil_div(n, kAdamTileElems);
-    const dim3 grid{unsigned(blocks)};
-    const uint16_t* g16 = static_cast<const uint16_t*>(grad);
-    uint16_t* p16o = static_cast<uint16_t*>(param_out);
+    const dim3 grid{unsigned(blocks), unsigned(owners)};
+    const AdamArgs a{master, m, v, static_cast<const uint16_t*>(grad), static_cast<uint16_t*>(param_out),
+                     AdamStrides{owners > 1 ? state_stride : 0, owners > 1 ? grad_stride : 0,
+                                 owners > 1 ? param_stride : 0},
+                     coef_dev, const_cast<int32_t*>(flag)};
+    return hip_status(launch_adam(grad_dtype, param_dtype, grid, s, sp, a, src), fn);
+}
+
+// zero_reduce_shard / zero_reduce_owners: the checks and the launch, owners
+// o = 0..owners-1 writing partial sets set + o (fn names the entry point).
+int reduce_enqueue(const char* fn, const void* const* contribs, int nd, int64_t n, int owners,
+                   int64_t contrib_stride, int dtype, float inv_loss_scale, void* reduced_out,
+                   int64_t reduced_stride, void* workspace, int64_t workspace_bytes, int set, int32_t* flag,
+                   void* stream) {
+    if (nd < 1 || nd > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": nd must be in [1, 1024]");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
+    if (owners < 1 || owners > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": owners must be in [1, 1024]");
+    if (owners > 1 && (contrib_stride < 0 || reduced_stride < n || contrib_stride > kMaxOwnerStride ||
+                       reduced_stride > kMaxOwnerStride))
+        return fail(ZERO_EINVAL, std::string(fn) + ": owner strides must be in [0, 2^40] (contributions) and "
+                                                   "[n, 2^40] (output)");
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
+    if (!pow2_positive(inv_loss_scale))
+        return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
+    if (set < 0 || set + owners > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": set out of range");
+    if (workspace == nullptr || (addr(workspace) & 7))
+        return fail(ZERO_EINVAL, std::string(fn) + ": workspace NULL or not 8-byte aligned");
+    if (workspace_bytes < zero_workspace_bytes(n, set + owners))
+        return fail(ZERO_EINVAL, std::string(fn) + ": workspace too small");
+    if (flag == nullptr || (addr(flag) & 3)) return fail(ZERO_EINVAL, std::string(fn) + ": flag NULL or misaligned");
+    const int64_t bytes = owners_extent(owners, reduced_stride, n, 2);        // all owners' outputs
+    const int64_t cbytes = owners_extent(owners, contrib_stride, n, 2);       // one rank's contributions
+    if (n > 0) {
+        if (contribs == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": contribs is NULL");
+        if (reduced_out == nullptr || (addr(reduced_out) & 1))
+            return fail(ZERO_EINVAL, std::string(fn) + ": reduced_out NULL or misaligned");
+        for (int r = 0; r < nd; ++r) {
+            if (contribs[r] == nullptr || (addr(contribs[r]) & 1))
+                return fail(ZERO_EINVAL, std::string(fn) + ": contribution " + std::to_string(r) + " NULL or misaligned");
+            if (overlaps(contribs[r], cbytes, reduced_out, bytes))
+                return fail(ZERO_EALIAS, std::string(fn) + ": reduced_out overlaps contribution " + std::to_string(r));
+            if (overlaps(contribs[r], cbytes, workspace, workspace_bytes))
+                return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps contribution " + std::to_string(r));
+        }
+        if (overlaps(reduced_out, bytes, workspace, workspace_bytes))
+            return fail(ZERO_EALIAS, std::string(fn) + ": reduced_out overlaps the workspace");
+        if (overlaps(reduced_out, bytes, flag, 4) || overlaps(workspace, workspace_bytes, flag, 4))
+            return fail(ZERO_EALIAS, std::string(fn) + ": flag overlaps an output");
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t blocks = partial_blocks(n);
+    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kPartialsOffset) + int64_t(set) * blocks;
+    Ptrs64 tab{};
+    const uint16_t* const* dtab = nullptr;
+    std::vector<const void*> ptrs(nd, nullptr);
+    if (n > 0) {
+        for (int r = 0; r < nd; ++r) ptrs[r] = contribs[r];
+    }
+    if (nd <= 64) {
+        for (int r = 0; r < nd; ++r) tab.p[r] = static_cast<const uint16_t*>(ptrs[r]);
+    } else {
+        // The runtime stages a pageable source before returning, so `ptrs`
+        // may go out of scope once the call is back.
+        if (int rc = refuse_capture(s, fn)) return rc;
+        dtab = static_cast<const uint16_t* const*>(workspace);
+        const hipError_t e = hipMemcpyAsync(workspace, ptrs.data(), sizeof(void*) * nd, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    std::vector<const void*> all16(ptrs);
+    all16.push_back(reduced_out);
+    const int64_t strides[2] = {contrib_stride, reduced_stride};
+    const Span sp = owners_span(make_span(n, all16.data(), int(all16.size()), nullptr, 0), owners, strides, 2);
+    const OwnerStrides os{owners > 1 ? contrib_stride : 0, owners > 1 ? reduced_stride : 0, owners > 1 ? blocks : 0};
+    int e2;
+    const bool pow2 = std::frexp(double(nd), &e2) == 0.5;
+    const float inv_nd = pow2 ? 1.0f / float(nd) : 0.0f;
+    const dim3 grid{unsigned(blocks), unsigned(owners)};
     const hipError_t e =
-        grad_dtype == ZERO_F16
-            ? launch_adam<ZERO_F16>(param_dtype, c_dev, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o)
-            : launch_adam<ZERO_BF16>(param_dtype, c_dev, grid, s, master, m, v, g16, sp, c, coef_dev, flag, p16o);
+        dtype == ZERO_F16
+            ? launch_reduce<ZERO_F16>(nd, grid, s, tab, dtab, sp, os, inv_nd, float(nd), pow2, inv_loss_scale,
+                                      static_cast<uint16_t*>(reduced_out), partials, flag)
+            : launch_reduce<ZERO_BF16>(nd, grid, s, tab, dtab, sp, os, inv_nd, float(nd), pow2, inv_loss_scale,
+                                       static_cast<uint16_t*>(reduced_out), partials, flag);
     return hip_status(e, fn);
 }
 
@@ -735,70 +923,15 @@ extern "C" {
 int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype, float inv_loss_scale,
                       void* reduced_out, void* workspace, int64_t workspace_bytes, int set,
                       int32_t* flag, void* stream) {
-    const char* fn = "zero_reduce_shard";
-    if (nd < 1 || nd > ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": nd must be in [1, 1024]");
-    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
-    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, std::string(fn) + ": dtype must be ZERO_F16 or ZERO_BF16");
-    if (!pow2_positive(inv_loss_scale))
-        return fail(ZERO_EINVAL, std::string(fn) + ": inv_loss_scale must be a positive power of two");
-    if (set < 0 || set >= ZERO_MAX_RANKS) return fail(ZERO_EINVAL, std::string(fn) + ": set out of range");
-    if (workspace == nullptr || (addr(workspace) & 7))
-        return fail(ZERO_EINVAL, std::string(fn) + ": workspace NULL or not 8-byte aligned");
-    if (workspace_bytes < zero_workspace_bytes(n, set + 1))
-        return fail(ZERO_EINVAL, std::string(fn) + ": workspace too small");
-    if (flag == nullptr || (addr(flag) & 3)) return fail(ZERO_EINVAL, std::string(fn) + ": flag NULL or misaligned");
-    const int64_t bytes = 2 * n;
-    if (n > 0) {
-        if (contribs == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": contribs is NULL");
-        if (reduced_out == nullptr || (addr(reduced_out) & 1))
-            return fail(ZERO_EINVAL, std::string(fn) + ": reduced_out NULL or misaligned");
-        for (int r = 0; r < nd; ++r) {
-            if (contribs[r] == nullptr || (addr(contribs[r]) & 1))
-                return fail(ZERO_EINVAL, std::string(fn) + ": contribution " + std::to_string(r) + " NULL or misaligned");
-            if (overlaps(contribs[r], bytes, reduced_out, bytes))
-                return fail(ZERO_EALIAS, std::string(fn) + ": reduced_out overlaps contribution " + std::to_string(r));
-            if (overlaps(contribs[r], bytes, workspace, workspace_bytes))
-                return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps contribution " + std::to_string(r));
-        }
-        if (overlaps(reduced_out, bytes, workspace, workspace_bytes))
-            return fail(ZERO_EALIAS, std::string(fn) + ": reduced_out overlaps the workspace");
-        if (overlaps(reduced_out, bytes, flag, 4) || overlaps(workspace, workspace_bytes, flag, 4))
-            return fail(ZERO_EALIAS, std::string(fn) + ": flag overlaps an output");
-    }
+    return reduce_enqueue("zero_reduce_shard", contribs, nd, n, 1, 0, dtype, inv_loss_scale, reduced_out, 0,
+                          workspace, workspace_bytes, set, flag, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t blocks = partial_blocks(n);
-    double* partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + kPartialsOffset) + int64_t(set) * blocks;
-    Ptrs64 tab{};
-    const uint16_t* const* dtab = nullptr;
-    std::vector<const void*> ptrs(nd, nullptr);
-    if (n > 0) {
-        for (int r = 0; r < nd; ++r) ptrs[r] = contribs[r];
-    }
-    if (nd <= 64) {
-        for (int r = 0; r < nd; ++r) tab.p[r] = static_cast<const uint16_t*>(ptrs[r]);
-    } else {
-        // The runtime stages a pageable source before returning, so `ptrs`
-        // may go out of scope once the call is back.
-        if (int rc = refuse_capture(s, fn)) return rc;
-        dtab = static_cast<const uint16_t* const*>(workspace);
-        const hipError_t e = hipMemcpyAsync(workspace, ptrs.data(), sizeof(void*) * nd, hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return hip_status(e, fn);
-    }
-    std::vector<const void*> all16(ptrs);
-    all16.push_back(reduced_out);
-    const Span sp = make_span(n, all16.data(), int(all16.size()), nullptr, 0);
-    int e2;
-    const bool pow2 = std::frexp(double(nd), &e2) == 0.5;
-    const float inv_nd = pow2 ? 1.0f / float(nd) : 0.0f;
-    const dim3 grid{unsigned(blocks)};
-    const hipError_t e =
-        dtype == ZERO_F16
-            ? launch_reduce<ZERO_F16>(nd, grid, s, tab, dtab, sp, inv_nd, float(nd), pow2, inv_loss_scale,
-                                      static_cast<uint16_t*>(reduced_out), partials, flag)
-            : launch_reduce<ZERO_BF16>(nd, grid, s, tab, dtab, sp, inv_nd, float(nd), pow2, inv_loss_scale,
-                                       static_cast<uint16_t*>(reduced_out), partials, flag);
-    return hip_status(e, fn);
+int zero_reduce_owners(const void* const* contribs, int nd, int64_t n, int owners, int64_t contrib_stride,
+                       int dtype, float inv_loss_scale, void* reduced_out, int64_t reduced_stride, void* workspace,
+                       int64_t workspace_bytes, int32_t* flag, void* stream) {
+    return reduce_enqueue("zero_reduce_owners", contribs, nd, n, owners, contrib_stride, dtype, inv_loss_scale,
+                          reduced_out, reduced_stride, workspace, workspace_bytes, 0, flag, stream);
 }
 
 int zero_grad_norm(const void* grad, int64_t n, int dtype, float inv_loss_scale, void* workspace,
@@ -825,10 +958,10 @@ int zero_adam_step(float* master, float* m, float* v, const void* grad, int grad
                    const zero_adam_hparams* hp, const float* coef_dev, const int32_t* flag,
                    void* param_out, int param_dtype, void* stream) {
     const char* fn = "zero_adam_step";
-    AdamConsts c;
-    if (int rc = adam_consts(fn, hp, &c)) return rc;
-    return adam_enqueue(fn, master, m, v, grad, grad_dtype, n, c, nullptr, coef_dev, flag, param_out, param_dtype,
-                        stream);
+    AdamSource src{kConstsArg, {}, nullptr, 0, nullptr};
+    if (int rc = adam_consts(fn, hp, &src.arg)) return rc;
+    return adam_enqueue(fn, master, m, v, 0, grad, grad_dtype, 0, n, 1, param_out, 0, param_dtype, src, coef_dev,
+                        flag, stream);
 }
 
 int zero_adam_consts_fill(const zero_adam_hparams* hp, zero_adam_consts* out) {
@@ -846,10 +979,35 @@ int zero_adam_step_consts(float* master, float* m, float* v, const void* grad, i
     const char* fn = "zero_adam_step_consts";
     if (consts_dev == nullptr || (addr(consts_dev) & 3))
         return fail(ZERO_EINVAL, std::string(fn) + ": consts_dev NULL or not 4-byte aligned");
-    const AdamConsts unused{};
-    return adam_enqueue(fn, master, m, v, grad, grad_dtype, n, unused,
-                        reinterpret_cast<const AdamConsts*>(consts_dev), coef_dev, flag, param_out, param_dtype,
-                        stream);
+    const AdamSource src{kConstsDevice, {}, reinterpret_cast<const AdamConsts*>(consts_dev), 1, nullptr};
+    return adam_enqueue(fn, master, m, v, 0, grad, grad_dtype, 0, n, 1, param_out, 0, param_dtype, src, coef_dev,
+                        flag, stream);
+}
+
+int zero_adam_step_owners(float* master, float* m, float* v, int64_t state_stride, const void* grad,
+                          int grad_dtype, int64_t grad_stride, int64_t n, int owners,
+                          const zero_adam_consts* table_dev, int64_t table_len, const zero_step_state* state_dev,
+                          const float* coef_dev, int32_t* flag, void* param_out, int64_t param_stride,
+                          int param_dtype, void* stream) {
+    const char* fn = "zero_adam_step_owners";
+    if (table_dev == nullptr || (addr(table_dev) & 3) || table_len < 1 || table_len > (int64_t(1) << 31))
+        return fail(ZERO_EINVAL, std::string(fn) + ": table_dev NULL or misaligned, or table_len not in [1, 2^31]");
+    if (state_dev == nullptr || (addr(state_dev) & 7))
+        return fail(ZERO_EINVAL, std::string(fn) + ": state_dev NULL or not 8-byte aligned");
+    const AdamSource src{kConstsTable, {}, reinterpret_cast<const AdamConsts*>(table_dev), table_len, state_dev};
+    return adam_enqueue(fn, master, m, v, state_stride, grad, grad_dtype, grad_stride, n, owners, param_out,
+                        param_stride, param_dtype, src, coef_dev, flag, stream);
+}
+
+int zero_step_end(int32_t* flag, zero_step_state* state_dev, void* stream) {
+    const char* fn = "zero_step_end";
+    if (flag == nullptr || (addr(flag) & 3)) return fail(ZERO_EINVAL, std::string(fn) + ": flag NULL or misaligned");
+    if (state_dev == nullptr || (addr(state_dev) & 7))
+        return fail(ZERO_EINVAL, std::string(fn) + ": state_dev NULL or not 8-byte aligned");
+    if (overlaps(flag, 4, state_dev, int64_t(sizeof(zero_step_state))))
+        return fail(ZERO_EALIAS, std::string(fn) + ": flag overlaps the step state");
+    return hip_status(launch(step_end_kernel, dim3(1), dim3(64), static_cast<hipStream_t>(stream), flag, state_dev),
+                      fn);
 }
 
 int zero_gather_params(const zero_plan* plan, const void* const* shards, int unit_begin, int unit_end,

@@ -3,11 +3,13 @@
 ``RankStep`` allocates the device buffers a workload needs (caller-owned, as
 the ABI requires), fills them from the seeded generators, and runs steps:
 
-    flag = 0
-    reduce each emulated owner's slice            zero_reduce_shard   (a1)
+    reduce each emulated owner's slice            zero_reduce_shard, or
+                                                  zero_reduce_owners (all owners, one launch)  (a1)
     norm + clip multiplier over all owners        zero_grad_norm      (a2)
-    AdamW + 16-bit cast into the parameter buffer zero_adam_step      (a3)
+    AdamW + 16-bit cast into the parameter buffer zero_adam_step_owners (a3)
     per-unit gather of every rank's 16-bit shard  zero_gather_params  (a4)
+    close the step: advance t if it was applied,
+    clear the flag                                zero_step_end
 
 With a block-quantised gather (ZeRO++ quantised weights) the last step is
 
@@ -22,10 +24,16 @@ With ZeRO-Offload the fp32 state is in host memory and the AdamW step is
 
 All calls go to one stream with no host synchronisation inside a step
 (except the offloaded update, which waits for its copies): the clip
-multiplier and the skip flag stay in device memory.  Contributions of the
-emulated ranks are buffers in this GPU's memory (one process, one GPU).
+multiplier, the skip flag and the step count stay in device memory.  AdamW
+takes its scalars from a device table of one zero_adam_consts per step,
+indexed by the device step count, which only applied steps advance; so a
+step skipped for a non-finite gradient leaves the bias corrections of the
+next one unchanged, and a captured step replays with no host work at all.
+Contributions of the emulated ranks are buffers in this GPU's memory (one
+process, one GPU).
 """
 
+import ctypes
 import os
 
 import torch
@@ -33,6 +41,7 @@ import torch
 from . import abi, synth
 
 OFFLOAD_CHUNK = 1 << 23          # values per staging slot of the offloaded update
+CONSTS_TABLE_LEN = 1024          # steps of AdamW scalars held on the device at a time
 CONTRIB_ROW_ALIGN = 2048         # 16-bit elements: 4 KiB
 HOST_THREADS_MAX = 16
 
@@ -44,7 +53,6 @@ class RankStep:
         self.w = w
         self.seed = seed
         self.device = device
-        self.t = 1
         self.plan = abi.Plan(w.units, w.nd, w.stage, w.align)
         self.n, _ = self.plan.rank(0)
         self.full_numel = self.plan.full_numel()
@@ -153,6 +161,19 @@ class RankStep:
         self.norm = torch.zeros(1, dtype=torch.float64, device=dev)
         self.coef = torch.zeros(1, dtype=torch.float32, device=dev)
 
+        # All owners' contributions in one launch when every rank's full local
+        # gradient is a row of one block (owner o's slice at o * n).
+        self.owners_table = None
+        if self.local is not None and len(self.owners) > 1:
+            self.owners_table = abi.PointerTable(list(self.local), 2 * self.full_numel, "contribution")
+
+        # The device step count (a zero_step_state) and the AdamW scalars of
+        # CONSTS_TABLE_LEN consecutive steps from state.table_t0.
+        self.state = torch.zeros(ctypes.sizeof(abi.zero_step_state) // 8, dtype=torch.int64, device=dev)
+        n_fields = len(abi.zero_adam_consts._fields_)
+        self.consts_table = torch.zeros((CONSTS_TABLE_LEN, n_fields), dtype=torch.float32, device=dev)
+        self._set_step(1)
+
     # -- inputs --------------------------------------------------------------
 
     def _zero_padding(self, owner, t):
@@ -195,11 +216,66 @@ class RankStep:
 
     # -- the step ------------------------------------------------------------
 
-    def hparams(self):
+    # -- the step count, on the device ------------------------------------------
+
+    def hparams_at(self, t):
         w = self.w
-        return abi.adam_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.inv_loss_scale, self.t)
+        return abi.adam_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.inv_loss_scale, t)
+
+    def hparams(self):
+        return self.hparams_at(self.t)
+
+    def _fill_table(self, t0):
+        rows = b"".join(bytes(abi.zero_adam_consts_fill(self.hparams_at(t))) for t in range(t0, t0 + CONSTS_TABLE_LEN))
+        # from pageable host memory: the copy is done before this returns
+        self.consts_table.copy_(torch.frombuffer(bytearray(rows), dtype=torch.float32).view_as(self.consts_table))
+
+    def _set_step(self, t):
+        """Set the device step count to t (counters cleared) and the scalars table from t."""
+        torch.cuda.synchronize(self.device)
+        self._fill_table(t)
+        self.state.copy_(torch.frombuffer(bytearray(abi.step_state(t, t)), dtype=torch.int64))
+        self._table_t0 = t
+        self._step_hi = t        # the device step count is at most this
+
+    def _ensure_table(self):
+        """Before enqueueing a step: the table must hold the step's scalars.
+
+        Each step advances the device count by at most one, so the count is at
+        most _step_hi; when that may pass the table's end, wait for the device,
+        read the count and refill the table from there.
+        """
+        if self._step_hi < self._table_t0 + CONSTS_TABLE_LEN:
+            return
+        torch.cuda.synchronize(self.device)
+        t = int(self.state[0].item())
+        self._fill_table(t)
+        self.state[3] = t
+        self._table_t0 = t
+        self._step_hi = t
+
+    @property
+    def t(self):
+        """The step count of the next update (read from the device)."""
+        return int(self.state[0].item())
+
+    @t.setter
+    def t(self, value):
+        self._set_step(int(value))
+
+    def counters(self):
+        """(t, applied, skipped, last_flag) from the device step state."""
+        st = [int(x) for x in self.state.cpu()]
+        last = st[4] & 0xFFFFFFFF               # the low half: last_flag (little-endian)
+        return st[0], st[1], st[2], last - (1 << 32) if last >= 1 << 31 else last
+
+    # -- the step ------------------------------------------------------------
 
     def reduce_all(self, stream=None):
+        if self.owners_table is not None:
+            abi.zero_reduce_owners(self.owners_table, self.n, len(self.owners), self.n, self.w.grad_dtype,
+                                   self.w.inv_loss_scale, self.reduced, self.n, self.ws, self.flag, stream)
+            return
         for i in range(len(self.owners)):
             abi.zero_reduce_shard(self.contrib_tables[i], self.n, self.w.grad_dtype, self.w.inv_loss_scale,
                                   self.reduced[i], self.ws, i, self.flag, stream)
@@ -210,21 +286,32 @@ class RankStep:
         abi.zero_grad_norm(grad, self.n, w.grad_dtype, w.inv_loss_scale, self.ws, self.n_sets, None, 0,
                            w.max_norm, self.flag, self.norm, self.coef, stream)
 
-    def adam_all(self, stream=None, consts_dev=None):
+    def adam_all(self, stream=None):
         w = self.w
-        hp = self.hparams()
-        for i in range(len(self.owners)):
-            if consts_dev is not None:
-                abi.zero_adam_step_consts(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype,
-                                          self.n, consts_dev, self.coef, self.flag, self.param_out(i),
-                                          w.param_dtype, stream)
-            elif w.offload:
+        k = len(self.owners)
+        if w.offload:
+            hp = self.hparams()
+            for i in range(k):
                 abi.zero_offload_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype,
                                            self.n, hp, self.coef, self.flag, self.param_out(i), w.param_dtype,
                                            self.staging, self.host_threads, stream)
-            else:
-                abi.zero_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype, self.n,
-                                   hp, self.coef, self.flag, self.param_out(i), w.param_dtype, stream)
+            return
+        # Every owner in one launch: owner i's rows are i * n apart in every array
+        # (the state, the reduced gradients, and the parameter buffer, where
+        # owners 0..nd-1 are consecutive); one owner needs no strides.
+        if k > 1:
+            # all ranks emulated: owners 0..nd-1, rows of the [k, n] arrays and
+            # consecutive slices of the parameter buffer (or rows of the shards)
+            grad, param, stride = self.reduced, self.full if self.shards is None else self.shards, self.n
+        else:
+            grad, param, stride = self.grad_of(0), self.param_out(0), 0
+        abi.zero_adam_step_owners(self.master, self.m, self.v, stride, grad, w.grad_dtype, stride, self.n, k,
+                                  self.consts_table, CONSTS_TABLE_LEN, self.state, self.coef, self.flag, param,
+                                  stride, w.param_dtype, stream)
+
+    def end_step(self, stream=None):
+        abi.zero_step_end(self.flag, self.state, stream)
+        self._step_hi += 1
 
     def quantize_shard(self, r, stream=None):
         abi.zero_quantize_blocks(self.shards[r], self.w.param_dtype, self.n, self.w.gather_bits, self.codes[r],
@@ -246,45 +333,48 @@ class RankStep:
         for u in range(self.n_units):
             self.gather_unit(u, stream)
 
-    def _enqueue(self, stream=None, consts_dev=None):
-        self.flag.zero_()
+    def _enqueue(self, stream=None):
         if not self.w.pre_reduced:
             self.reduce_all(stream)
         self.norm_all(stream)
-        self.adam_all(stream, consts_dev)
+        self.adam_all(stream)
         if self.codes is not None:
             self.quantize_all(stream)
         if self.shards is not None:
             self.gather_all(stream)
+        self.end_step(stream)
 
     def step(self, stream=None):
-        """Enqueue one whole step; returns without synchronising."""
+        """Enqueue one whole step; returns without synchronising.
+
+        The flag starts each step cleared (by the previous step's end); a set
+        flag skips the update and leaves the step count where it was.
+        """
+        self._ensure_table()
         self._enqueue(stream)
-        self.t += 1
 
     # -- the step as a HIP graph -----------------------------------------------
 
     def capture(self):
         """Capture one whole step as a HIP graph (no host work inside a step).
 
-        AdamW then reads its scalars (step count, bias corrections) from a
-        device buffer that replay() refreshes before each launch of the graph.
+        AdamW reads its scalars from the device table by the device step count,
+        so replays need no host refresh.
         """
         if self.w.offload:
             raise ValueError("the offloaded update runs on the host and cannot be captured")
-        self.consts_dev = torch.zeros(len(abi.zero_adam_consts._fields_), dtype=torch.float32, device=self.device)
+        self._ensure_table()
         self.graph = torch.cuda.CUDAGraph()
+        hi = self._step_hi
         with torch.cuda.graph(self.graph):
-            self._enqueue(consts_dev=self.consts_dev)
+            self._enqueue()
+        self._step_hi = hi       # capturing ran nothing
 
     def replay(self):
-        """Launch the captured step for the current step count; returns without synchronising."""
-        c = abi.zero_adam_consts_fill(self.hparams())
-        # from pageable host memory: the runtime stages the 40 bytes before the
-        # call returns, so consecutive replays never see each other's values
-        self.consts_dev.copy_(torch.frombuffer(bytearray(c), dtype=torch.float32))
+        """Launch the captured step; returns without synchronising."""
+        self._ensure_table()
         self.graph.replay()
-        self.t += 1
+        self._step_hi += 1
 
     # -- accounting ------------------------------------------------------------
 
@@ -311,9 +401,12 @@ def phase_model(w, plan):
     n, _ = plan.rank(0)
     n_units = plan.info()["n_units"]
     owners = w.nd if w.all_ranks else 1
+    # every owner in one launch when all ranks' local gradients are rows of one block
+    reduce_launches = 1 if w.all_ranks and n_units == 1 else owners
     out = {}
     if not w.pre_reduced:
-        out["reduce"] = {"kernel": "reduce_kernel", "launches": owners, "bytes_per_launch": (2 * w.nd + 2) * n}
+        out["reduce"] = {"kernel": "reduce_kernel", "launches": reduce_launches,
+                         "bytes_per_launch": (2 * w.nd + 2) * n * owners / reduce_launches}
     out["norm"] = {"kernel": "sumsq_kernel" if w.pre_reduced else "finalize_kernel", "launches": 1,
                    "bytes_per_launch": 2 * n if w.pre_reduced else 0}
     if w.offload:
@@ -321,7 +414,7 @@ def phase_model(w, plan):
         # the 4 bytes per element over PCIe are reported separately
         out["adam"] = {"kernel": "host_adam", "launches": owners, "bytes_per_launch": 28 * n}
     else:
-        out["adam"] = {"kernel": "adam_kernel", "launches": owners, "bytes_per_launch": 28 * n}
+        out["adam"] = {"kernel": "adam_kernel", "launches": 1, "bytes_per_launch": 28 * n * owners}
     if w.gather_bits != 16:
         code = abi.zero_quant_code_bytes(n, w.gather_bits) + 4 * abi.zero_quant_scale_count(n)
         # shards are 16-byte aligned, so the span kernel runs
