@@ -107,6 +107,14 @@ def cpu_baseline(run, budget_s=12.0):
         return contribs, grad, state
 
     samples = [inputs(o) for o in offsets]
+    # The reduce writes in place over the rank's own contribution, so the
+    # device's reduce of these very inputs is the next step's output.
+    device_reduced = None
+    if not w.pre_reduced:
+        import torch
+        run.step()
+        torch.cuda.synchronize()
+        device_reduced = synth.bits(run.reduced[0, offsets[0]:offsets[0] + chunk])
     counts = [0] * threads
     first_reduced = [None]
     stop = time.perf_counter() + budget_s
@@ -142,9 +150,8 @@ def cpu_baseline(run, budget_s=12.0):
         t.join()
     dt = time.perf_counter() - t0
     parity = None
-    if not w.pre_reduced:
-        o = offsets[0]
-        parity = bool(np.array_equal(first_reduced[0], synth.bits(run.reduced[0, o:o + chunk])))
+    if device_reduced is not None:
+        parity = bool(np.array_equal(first_reduced[0], device_reduced))
     return {
         "value": sum(counts) / dt,
         "unit": "params/s",

@@ -204,7 +204,10 @@ int64_t zero_workspace_bytes(int64_t n, int n_sets);
  *
  * contribs: HOST array of nd device pointers, each to n 16-bit values of
  *   `dtype` (rank 0 first).  1 <= nd <= 1024.
- * reduced_out: device, n values of `dtype`; may not overlap any contribution.
+ * reduced_out: device, n values of `dtype`.  It may be exactly one of the
+ *   contributions (the reduce in place, as a rank keeps the reduced slice in
+ *   its own gradient buffer: each element is read from every rank before it
+ *   is written); otherwise it may not overlap any contribution.
  * inv_loss_scale: a positive power of two (1 when no loss scaling).
  * workspace / workspace_bytes: >= zero_workspace_bytes(n, set + 1).
  * flag: device int32.
@@ -224,7 +227,9 @@ int zero_reduce_shard(const void* const* contribs, int nd, int64_t n, int dtype,
  * with set = o, bit for bit.
  *
  * 1 <= owners <= 1024; with owners > 1, 0 <= contrib_stride <= 2^40 and
- * n <= reduced_stride <= 2^40 (owners' outputs do not overlap).  Strides
+ * n <= reduced_stride <= 2^40 (owners' outputs do not overlap).  In place
+ * as for zero_reduce_shard: reduced_out == contribs[k] with reduced_stride ==
+ * contrib_stride.  Strides
  * that are multiples of 4 keep the vector path.  workspace_bytes >=
  * zero_workspace_bytes(n, owners).  Other arguments and errors as
  * zero_reduce_shard.

@@ -92,6 +92,10 @@ def test_step_after_restore_equals_uninterrupted(abi, tmp_path):
     for k, (x, y) in enumerate(zip((a.master, a.m, a.v), (b.master, b.m, b.v))):
         assert np.array_equal(_bits32(x[0, :real]), _bits32(y[0, :real])), k
         assert not y[0, real:].any()
+    # step 2's gradients are inputs, not state: give both the same (a's reduce
+    # wrote its average in place over its own contribution)
+    for x, y in zip(a.contribs(0), b.contribs(0)):
+        y.copy_(x)
     a.step()
     b.step()
     torch.cuda.synchronize()

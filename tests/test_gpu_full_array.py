@@ -115,7 +115,7 @@ def test_full_shard_zero3_and_gathered_layers(runner):
     contribs = [_host16(c) for c in run.contribs(0)]
     state0 = [t[0].cpu().numpy().copy() for t in (run.master, run.m, run.v)]
     layers = [0, 17, 30, len(plan.units) - 1]
-    others = {u: [_host16(run.shards[r, plan.units[u].shard_base:plan.units[u].shard_base + plan.units[u].slice_numel])
+    others = {u: [_host16(run.shards[r][plan.units[u].shard_base:plan.units[u].shard_base + plan.units[u].slice_numel])
                   for r in range(w.nd)] for u in layers}
     _note(f"full-shard: step over n={n}, oracle on {THREADS} threads")
     run.step()

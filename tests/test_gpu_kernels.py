@@ -210,6 +210,31 @@ def test_reduce_is_deterministic(abi):
     assert norms[0] == norms[1] == norms[2]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nd, k, n, offset", [(4, 0, 300_001, 0), (8, 7, 4099, 0), (3, 1, 100_003, 3),
+                                               (64, 30, 20_000, 1), (100, 99, 5_001, 0)])
+def test_reduce_in_place_over_one_contribution(abi, dtype, nd, k, n, offset):
+    # reduced_out may be contribution k itself: each element is read from every
+    # rank before it is written, so the result is the oracle's, and the other
+    # contributions are untouched.
+    _note(f"reduce in place dtype={dtype} nd={nd} k={k} n={n} offset={offset}")
+    rng = np.random.default_rng(nd * 31 + k + n)
+    contribs = [_rand16(rng, n, 1e-3, dtype) for _ in range(nd)]
+    ref, bad = step.reduce_shard(contribs, dtype)
+    dev = [_dev16(c, dtype, offset=offset) for c in contribs]
+    ws = _ws(abi, n, 1)
+    flag, norm, coef = _scalars()
+    abi.zero_reduce_shard(dev, n, dtype, 1.0, dev[k], ws, 0, flag)
+    abi.zero_grad_norm(None, n, dtype, 1.0, ws, 1, None, 0, 1.0, flag, norm, coef)
+    torch.cuda.synchronize()
+    assert not bad and int(flag.item()) == 0
+    assert np.array_equal(_bits(dev[k]), ref)
+    for r in range(nd):
+        if r != k:
+            assert np.array_equal(_bits(dev[r]), contribs[r]), r
+    norm_ok(norm.item(), step.norm_from_sumsq(step.sumsq_exact(ref, dtype)), n)
+
+
 @pytest.mark.parametrize("n, sets", [(20_000_003, 1), (5_000_001, 4)])
 def test_norm_two_stage_finalize(abi, n, sets):
     # More than 8192 partial sums: the finalize folds them in two stages.

@@ -148,7 +148,7 @@ def test_full_size_step(runner, name):
         chunks[o] = (contribs, grad, state)
     others = None
     if run.shards is not None:
-        others = {o: [synth.bits(run.shards[r, o:o + CHUNK]) for r in range(w.nd)] for o in offs}
+        others = {o: [synth.bits(run.shards[r][o:o + CHUNK]) for r in range(w.nd)] for o in offs}
     torch.cuda.synchronize()
 
     _note(f"full-size {name}: step over n={n}")

@@ -273,7 +273,7 @@ class Plan:
         self._cache = {}
 
     def close(self):
-        if self.handle:
+        if self.handle and lib is not None:          # the module may be torn down first at exit
             lib.zero_plan_destroy(self.handle)
             self.handle = _P()
 

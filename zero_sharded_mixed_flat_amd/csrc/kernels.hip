@@ -750,10 +750,14 @@ int reduce_enqueue(const char* fn, const void* const* contribs, int nd, int64_t 
         if (contribs == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": contribs is NULL");
         if (reduced_out == nullptr || (addr(reduced_out) & 1))
             return fail(ZERO_EINVAL, std::string(fn) + ": reduced_out NULL or misaligned");
+        // In place is allowed: reduced_out may be exactly one contribution
+        // (each element is read from every rank before it is written).
+        const bool same_layout = owners == 1 || reduced_stride == contrib_stride;
         for (int r = 0; r < nd; ++r) {
             if (contribs[r] == nullptr || (addr(contribs[r]) & 1))
                 return fail(ZERO_EINVAL, std::string(fn) + ": contribution " + std::to_string(r) + " NULL or misaligned");
-            if (overlaps(contribs[r], cbytes, reduced_out, bytes))
+            const bool in_place = contribs[r] == reduced_out && same_layout;
+            if (!in_place && overlaps(contribs[r], cbytes, reduced_out, bytes))
                 return fail(ZERO_EALIAS, std::string(fn) + ": reduced_out overlaps contribution " + std::to_string(r));
             if (overlaps(contribs[r], cbytes, workspace, workspace_bytes))
                 return fail(ZERO_EALIAS, std::string(fn) + ": workspace overlaps contribution " + std::to_string(r));

@@ -63,40 +63,60 @@ class RankStep:
         n = self.n
         dev = device
 
+        self.ledger = []          # (buffer, role, bytes) of every allocation, in order
+
         # Gradients.  With every rank emulated on one flat unit, each rank holds a
         # full local gradient and owner o's contribution from rank r is the slice
-        # [o*n, (o+1)*n) of rank r's gradient.  Otherwise only the owned slice of
-        # each rank's gradient exists, as an [nd, n] block in shard order.
+        # [o*n, (o+1)*n) of rank r's gradient.  Otherwise this rank's own gradient
+        # is the whole local gradient under ZeRO-0/1 (gradients are not sharded)
+        # or only its slice under ZeRO-2/3, and the other ranks' contributions to
+        # the slice are an [nd - 1, n] block standing in for their buffers.  The
+        # reduce writes the average in place over the rank's own contribution,
+        # where a rank keeps its reduced slice.
         self.local = None
         self.contrib_block = None
+        self.grad_full = None
+        self.own_grad = None
+        row = -(-n // CONTRIB_ROW_ALIGN) * CONTRIB_ROW_ALIGN
         if w.pre_reduced:
-            self.grad = synth.grad16(n, w.grad_dtype, w.grad_std * w.loss_scale, seed, 1, dev)
+            self.grad = self._keep("grad", "grads16",
+                                   synth.grad16(n, w.grad_dtype, w.grad_std * w.loss_scale, seed, 1, dev))
             if tile_period:
                 synth.tile_(self.grad, tile_period)
         elif w.all_ranks and self.n_units == 1:
-            self.local = torch.empty((w.nd, self.full_numel), dtype=gdt, device=dev)
+            self.local = self._keep("local", "all_ranks_grads16",
+                                    torch.empty((w.nd, self.full_numel), dtype=gdt, device=dev))
             self.fresh_gradients(step=0, tile_period=tile_period)
+            self.reduced = self._keep("reduced", "all_ranks_grads16",
+                                      torch.empty((len(self.owners), n), dtype=gdt, device=dev))
         else:
             # Rows start on 4 KiB boundaries, as separate (peer) buffers would:
             # a row stride of 2n bytes alone can leave every wave-wide access
             # straddling one more 128-byte line than it needs.
-            row = -(-n // CONTRIB_ROW_ALIGN) * CONTRIB_ROW_ALIGN
-            self.contrib_block = torch.empty((w.nd, row), dtype=gdt, device=dev)[:, :n]
-            for r in range(w.nd):
-                synth.normal_(self.contrib_block[r], w.grad_std * w.loss_scale, seed, 100 + r)
-                synth.outliers_(self.contrib_block[r], w.outlier_frac, w.outlier_mult, seed, 100 + r)
+            if w.nd > 1:
+                self.contrib_block = self._keep("peer_contributions", "peers",
+                                                torch.empty((w.nd - 1, row), dtype=gdt, device=dev))[:, :n]
+            if w.stage <= 1:
+                self.grad_full = self._keep("grad_full", "grads16",
+                                            torch.zeros(self.full_numel, dtype=gdt, device=dev))
+                self.own_grad = self.grad_full[w.rank * n:(w.rank + 1) * n]
+            else:
+                self.own_grad = self._keep("grad_own", "grads16", torch.empty(row, dtype=gdt, device=dev))[:n]
+            for r, c in enumerate(self.contribs(0)):
+                synth.normal_(c, w.grad_std * w.loss_scale, seed, 100 + r)
+                synth.outliers_(c, w.outlier_frac, w.outlier_mult, seed, 100 + r)
                 if tile_period:
-                    synth.tile_(self.contrib_block[r], tile_period)
-        if not w.pre_reduced:
-            self.reduced = torch.empty((len(self.owners), n), dtype=gdt, device=dev)
+                    synth.tile_(c, tile_period)
+            self.reduced = self.own_grad.view(1, n)
 
         # fp32 optimizer state, one shard per emulated owner (in host memory,
         # drawn on the GPU chunk by chunk, under ZeRO-Offload).
         k = len(self.owners)
         state_dev = "cpu" if w.offload else dev
-        self.master = torch.empty((k, n), dtype=torch.float32, device=state_dev)
-        self.m = torch.empty((k, n), dtype=torch.float32, device=state_dev)
-        self.v = torch.empty((k, n), dtype=torch.float32, device=state_dev)
+        role = ("all_ranks_" if k > 1 else "") + ("state32_host" if w.offload else "state32")
+        self.master = self._keep("master", role, torch.empty((k, n), dtype=torch.float32, device=state_dev))
+        self.m = self._keep("m", role, torch.empty((k, n), dtype=torch.float32, device=state_dev))
+        self.v = self._keep("v", role, torch.empty((k, n), dtype=torch.float32, device=state_dev))
         for i, o in enumerate(self.owners):
             synth.normal_(self.master[i], w.master_std, seed, 200 + o, via=dev)
             if w.m_std:
@@ -112,19 +132,29 @@ class RankStep:
 
         # 16-bit parameters.  ZeRO-1/2 write the owner's slice straight into the
         # full gather buffer; ZeRO-3 writes the owner's shard, then gathers every
-        # rank's shard unit by unit; a pre-reduced owner update writes its shard.
+        # rank's shard unit by unit into the full buffer (assembled layer by
+        # layer for compute); a pre-reduced owner update writes its shard.
         self.full = None
         self.shards = None
         if w.gather_per_unit:
-            self.shards = torch.empty((w.nd, n), dtype=pdt, device=dev)
+            if k > 1:
+                block = self._keep("shards", "all_ranks_params16", torch.empty((w.nd, n), dtype=pdt, device=dev))
+                self.shards = list(block)
+                self._shards_block = block
+            else:
+                own = self._keep("shard_own", "params16", torch.empty(n, dtype=pdt, device=dev))
+                peers = self._keep("peer_shards", "peers", torch.empty((w.nd - 1, n), dtype=pdt, device=dev))
+                self.shards = [peers[r if r < w.rank else r - 1] for r in range(w.nd) if r != w.rank]
+                self.shards.insert(w.rank, own)
             for r in range(w.nd):
                 if r not in self.owners:
                     synth.normal_(self.shards[r], w.gather_shard_std, seed, 500 + r)
-            self.full = torch.zeros(self.full_numel, dtype=pdt, device=dev)
+            self.full = self._keep("gathered", "gathered", torch.zeros(self.full_numel, dtype=pdt, device=dev))
         elif w.pre_reduced:
-            self.param = torch.zeros(n, dtype=pdt, device=dev)
+            self.param = self._keep("param", "params16", torch.zeros(n, dtype=pdt, device=dev))
         else:
-            self.full = torch.zeros(self.full_numel, dtype=pdt, device=dev)
+            self.full = self._keep("full", "all_ranks_params16" if k > 1 else "params16",
+                                   torch.zeros(self.full_numel, dtype=pdt, device=dev))
 
         # Block-quantised gather: codes and scales as every rank would send
         # them; the other ranks' come from quantising their synthetic 16-bit
@@ -132,8 +162,9 @@ class RankStep:
         self.codes = self.scales = None
         if w.gather_bits != 16:
             cb = abi.zero_quant_code_bytes(n, w.gather_bits)
-            self.codes = torch.empty((w.nd, cb), dtype=torch.uint8, device=dev)
-            self.scales = torch.empty((w.nd, abi.zero_quant_scale_count(n)), dtype=torch.float32, device=dev)
+            self.codes = self._keep("codes", "gather_codes", torch.empty((w.nd, cb), dtype=torch.uint8, device=dev))
+            self.scales = self._keep("scales", "gather_codes", torch.empty((w.nd, abi.zero_quant_scale_count(n)),
+                                                                            dtype=torch.float32, device=dev))
             for r in range(w.nd):
                 if r not in self.owners:
                     self.quantize_shard(r)
@@ -152,14 +183,16 @@ class RankStep:
         self.host_threads = min(HOST_THREADS_MAX, len(os.sched_getaffinity(0)))
         if w.offload:
             chunk = min(OFFLOAD_CHUNK, max(64, n))
-            self.staging = torch.empty(64 + 8 * chunk, dtype=torch.uint8, pin_memory=True)
+            self.staging = self._keep("staging", "staging_host",
+                                      torch.empty(64 + 8 * chunk, dtype=torch.uint8, pin_memory=True))
 
         n_sets = 1 if w.pre_reduced else len(self.owners)
-        self.ws = torch.empty(abi.zero_workspace_bytes(n, n_sets), dtype=torch.uint8, device=dev)
+        self.ws = self._keep("workspace", "work",
+                             torch.empty(abi.zero_workspace_bytes(n, n_sets), dtype=torch.uint8, device=dev))
         self.n_sets = n_sets
-        self.flag = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.norm = torch.zeros(1, dtype=torch.float64, device=dev)
-        self.coef = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.flag = self._keep("flag", "work", torch.zeros(1, dtype=torch.int32, device=dev))
+        self.norm = self._keep("norm", "work", torch.zeros(1, dtype=torch.float64, device=dev))
+        self.coef = self._keep("coef", "work", torch.zeros(1, dtype=torch.float32, device=dev))
 
         # All owners' contributions in one launch when every rank's full local
         # gradient is a row of one block (owner o's slice at o * n).
@@ -169,10 +202,20 @@ class RankStep:
 
         # The device step count (a zero_step_state) and the AdamW scalars of
         # CONSTS_TABLE_LEN consecutive steps from state.table_t0.
-        self.state = torch.zeros(ctypes.sizeof(abi.zero_step_state) // 8, dtype=torch.int64, device=dev)
+        self.state = self._keep("step_state", "work", torch.zeros(ctypes.sizeof(abi.zero_step_state) // 8,
+                                                                  dtype=torch.int64, device=dev))
         n_fields = len(abi.zero_adam_consts._fields_)
-        self.consts_table = torch.zeros((CONSTS_TABLE_LEN, n_fields), dtype=torch.float32, device=dev)
+        self.consts_table = self._keep("consts_table", "work", torch.zeros((CONSTS_TABLE_LEN, n_fields),
+                                                                         dtype=torch.float32, device=dev))
         self._set_step(1)
+        expect = allocation_plan(w, self.plan)
+        if self.ledger != expect:
+            raise AssertionError(f"allocations differ from allocation_plan: {self.ledger} vs {expect}")
+
+    def _keep(self, name, role, tensor):
+        """Record an allocation (its whole storage) in the ledger; returns the tensor."""
+        self.ledger.append((name, role, tensor.untyped_storage().nbytes()))
+        return tensor
 
     # -- inputs --------------------------------------------------------------
 
@@ -197,11 +240,13 @@ class RankStep:
             g[psi:].zero_()
 
     def contribs(self, i):
-        """Device views of the nd contributions to emulated owner i's slice."""
+        """Device views of the nd contributions to emulated owner i's slice (rank order)."""
         o = self.owners[i]
         if self.local is not None:
             return [self.local[r, o * self.n:(o + 1) * self.n] for r in range(self.w.nd)]
-        return [self.contrib_block[r] for r in range(self.w.nd)]
+        rank = self.w.rank
+        return [self.own_grad if r == rank else self.contrib_block[r if r < rank else r - 1]
+                for r in range(self.w.nd)]
 
     def param_out(self, i):
         o = self.owners[i]
@@ -302,7 +347,8 @@ class RankStep:
         if k > 1:
             # all ranks emulated: owners 0..nd-1, rows of the [k, n] arrays and
             # consecutive slices of the parameter buffer (or rows of the shards)
-            grad, param, stride = self.reduced, self.full if self.shards is None else self.shards, self.n
+            param = self.full if self.shards is None else self._shards_block
+            grad, stride = self.reduced, self.n
         else:
             grad, param, stride = self.grad_of(0), self.param_out(0), 0
         abi.zero_adam_step_owners(self.master, self.m, self.v, stride, grad, w.grad_dtype, stride, self.n, k,
@@ -424,3 +470,63 @@ def phase_model(w, plan):
     elif w.gather_per_unit:
         out["gather"] = {"kernel": "gather_kernel", "launches": n_units, "bytes_per_launch": 4 * n * w.nd / n_units}
     return out
+
+
+def allocation_plan(w, plan):
+    """Every allocation RankStep makes for workload ``w``: (buffer, role, bytes), in order.
+
+    Roles, for the emulated rank: "params16" its 16-bit parameters, "grads16"
+    its 16-bit gradients, "state32" (or "state32_host" under ZeRO-Offload) its
+    fp32 master, m and v; "peers" buffers standing in for the other ranks'
+    (their gradient contributions to this rank's slice, their 16-bit shards);
+    "gathered" the full 16-bit parameters a ZeRO-3 rank assembles layer by
+    layer for compute; "gather_codes" the quantised gather's codes and scales;
+    "work" workspace, flag, norm, clip multiplier, step state and scalars
+    table; "staging_host" pinned staging.  Roles prefixed "all_ranks_" belong
+    to every emulated rank at once.  RankStep checks its allocations against
+    this list, so it can be read without a GPU.  Needs no GPU.
+    """
+    n, _ = plan.rank(0)
+    full = plan.full_numel()
+    n_units = plan.info()["n_units"]
+    k = w.nd if w.all_ranks else 1
+    row = -(-n // CONTRIB_ROW_ALIGN) * CONTRIB_ROW_ALIGN
+    out = []
+    if w.pre_reduced:
+        out.append(("grad", "grads16", 2 * n))
+    elif w.all_ranks and n_units == 1:
+        out += [("local", "all_ranks_grads16", 2 * w.nd * full), ("reduced", "all_ranks_grads16", 2 * k * n)]
+    else:
+        if w.nd > 1:
+            out.append(("peer_contributions", "peers", 2 * (w.nd - 1) * row))
+        out.append(("grad_full", "grads16", 2 * full) if w.stage <= 1 else ("grad_own", "grads16", 2 * row))
+    role = ("all_ranks_" if k > 1 else "") + ("state32_host" if w.offload else "state32")
+    out += [(name, role, 4 * k * n) for name in ("master", "m", "v")]
+    if w.gather_per_unit:
+        if k > 1:
+            out.append(("shards", "all_ranks_params16", 2 * w.nd * n))
+        else:
+            out += [("shard_own", "params16", 2 * n), ("peer_shards", "peers", 2 * (w.nd - 1) * n)]
+        out.append(("gathered", "gathered", 2 * full))
+    elif w.pre_reduced:
+        out.append(("param", "params16", 2 * n))
+    else:
+        out.append(("full", "all_ranks_params16" if k > 1 else "params16", 2 * full))
+    if w.gather_bits != 16:
+        out += [("codes", "gather_codes", w.nd * abi.zero_quant_code_bytes(n, w.gather_bits)),
+                ("scales", "gather_codes", 4 * w.nd * abi.zero_quant_scale_count(n))]
+    if w.offload:
+        out.append(("staging", "staging_host", 64 + 8 * min(OFFLOAD_CHUNK, max(64, n))))
+    n_sets = 1 if w.pre_reduced else k
+    out += [("workspace", "work", abi.zero_workspace_bytes(n, n_sets)), ("flag", "work", 4), ("norm", "work", 8),
+            ("coef", "work", 4), ("step_state", "work", ctypes.sizeof(abi.zero_step_state)),
+            ("consts_table", "work", 4 * CONSTS_TABLE_LEN * len(abi.zero_adam_consts._fields_))]
+    return out
+
+
+def role_bytes(w, plan):
+    """Bytes per role of allocation_plan."""
+    totals = {}
+    for _, role, nbytes in allocation_plan(w, plan):
+        totals[role] = totals.get(role, 0) + nbytes
+    return totals
