@@ -492,6 +492,7 @@ def main():
 
     for _ in range(args.warmup):
         run.step()
+    run.flush()
     torch.cuda.synchronize()
     step_fn = run.step
     if args.graph:
@@ -511,6 +512,7 @@ def main():
             a.record()
             step_fn()
             b.record()
+        run.flush()
         torch.cuda.synchronize()
         cold = sorted(a.elapsed_time(b) for a, b in pairs)
         ms_per_step = cold[len(cold) // 2]
@@ -520,6 +522,7 @@ def main():
         t0 = time.perf_counter()
         for _ in range(args.steps):
             step_fn()
+        run.flush()                      # a delayed host update still in flight ends inside the timing
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_per_step = 1e3 * wall / args.steps
@@ -629,7 +632,8 @@ def main():
         roofline = {"bound": "host_dram", "peak": read_gbs,
                     "peak_source": f"measured host read bandwidth, {run.host_threads} threads (no published figure)"}
         adam_ms = kern_ms["adam"]
-        offload = {"host_threads": run.host_threads, "host_isa": ["scalar", "avx2", "avx512"][abi.zero_cpu_isa()],
+        offload = {"delayed_update": bool(w.offload_delay),
+                   "host_threads": run.host_threads, "host_isa": ["scalar", "avx2", "avx512"][abi.zero_cpu_isa()],
                    "host_adam_params_per_s": owned / (adam_ms * 1e-3),
                    "pcie_bytes_per_step": 4 * owned, "staging_bytes": run.staging.numel(),
                    "update_ms": adam_ms, "host_copy_gbs": host_gbs, "host_read_gbs": read_gbs, "cpu": cpu_model()}

@@ -619,6 +619,71 @@ int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_d
                            int param_dtype, void* staging, int64_t staging_bytes, int n_threads,
                            void* stream);
 
+/*
+ * The one-step-delayed update of ZeRO-Offload (L18 notes §4.4: the CPU's
+ * update of step t runs while the GPU already works on step t+1, so step
+ * t+1's forward and backward see the parameters of step t-1).  A
+ * zero_offload handle owns persistent host worker threads for the host
+ * AdamW.  Per step t, after its reduce and norm are enqueued:
+ *   zero_offload_end(step t-1)   -- waits for the update of step t-1 and
+ *                                   enqueues the copy of its 16-bit
+ *                                   parameters into param_dev;
+ *   zero_offload_begin(step t)   -- brings step t's clip multiplier and flag
+ *                                   to the host, copies its reduced gradient
+ *                                   aside on the device and returns; a thread
+ *                                   of the handle then streams that copy
+ *                                   through the host AdamW chunk by chunk (as
+ *                                   zero_offload_adam_step does), on a stream
+ *                                   of its own;
+ * so the GPU runs step t+1's reduce and norm while the host updates.  The
+ * updates are those of zero_cpu_adam_step, in the same order, so the state
+ * after any step equals the undelayed sequence bit for bit; only the
+ * parameters the device holds lag by one step.
+ *
+ * zero_offload_create: n_threads in [1, 256] workers.  Errors: ZERO_EINVAL,
+ * ZERO_ENOMEM.  zero_offload_destroy waits for an update in flight, then
+ * frees the handle (the parameters of that update are dropped).
+ */
+typedef struct zero_offload zero_offload;
+
+int zero_offload_create(int n_threads, zero_offload** out);
+void zero_offload_destroy(zero_offload* h);
+
+/*
+ * zero_offload_begin -- starts the update of one step.  On `stream` it copies
+ * *coef_dev and *flag_dev to the host and waits for them; a set flag (or
+ * n = 0) starts nothing.  Otherwise it enqueues a device copy of
+ * grad_dev[0..n) into the first 2n bytes of device_buffer (so the caller
+ * may overwrite grad_dev in later stream work) and returns; the update
+ * collects its 16-bit parameters in the next 2n bytes.
+ *
+ * master, m, v: host fp32, n each, distinct, updated in place.  staging:
+ * pinned host memory as for zero_offload_adam_step.  device_buffer:
+ * caller-owned device memory, >= 4n bytes, not overlapping grad_dev.  Until
+ * the matching zero_offload_end returns, the caller must not touch master,
+ * m, v, staging or device_buffer.  hp: as zero_cpu_adam_step.
+ * 0 <= n <= 2^34.  Errors (nothing started): ZERO_EINVAL (arguments; an
+ * update begun and not ended; a clip multiplier that is not finite and
+ * positive), ZERO_EALIAS, ZERO_EHIP.
+ */
+int zero_offload_begin(zero_offload* h, float* master, float* m, float* v, const void* grad_dev,
+                       int grad_dtype, int64_t n, const zero_adam_hparams* hp,
+                       const float* coef_dev, const int32_t* flag_dev, int param_dtype,
+                       void* device_buffer, int64_t device_bytes, void* staging,
+                       int64_t staging_bytes, void* stream);
+
+/*
+ * zero_offload_end -- finishes the update begun last: waits for its host
+ * AdamW and copies, then enqueues on `stream` the device copy of its 16-bit
+ * parameters (param_dtype of the begin call, n values) into param_dev.
+ * *applied (if not NULL) is 1 if the step was applied, 0 if it was skipped
+ * (nothing moves).  Errors: ZERO_EINVAL (no update begun; param_dev NULL or
+ * misaligned when the step was applied), ZERO_EHIP (including a copy or
+ * launch refused while the update was in flight: master, m and v are then
+ * partly updated).
+ */
+int zero_offload_end(zero_offload* h, void* param_dev, int* applied, void* stream);
+
 /* The host AdamW's instruction set in use (ZERO_CPU_*). */
 int zero_cpu_isa(void);
 

@@ -241,6 +241,27 @@ def test_step_end_rejects():
         assert e.value.code == code
 
 
+def test_offload_handle_rejects_before_any_copy():
+    h = abi.Offload(2)
+    n = 1024
+    args = dict(master=A, m=A + 4 * n, v=A + 8 * n, grad=B, grad_dtype="bf16", n=n,
+                hp=abi.adam_hparams(3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 1), coef=F, flag=F + 4, param_dtype="bf16",
+                device_buffer=W, staging=0x50000000, stream=0, device_bytes=4 * n, staging_bytes=4096)
+    for bad, code in ((dict(n=-1), abi.ZERO_EINVAL), (dict(device_bytes=4 * n - 2), abi.ZERO_EINVAL),
+                      (dict(staging_bytes=100), abi.ZERO_EINVAL), (dict(staging=0x50000008), abi.ZERO_EINVAL),
+                      (dict(device_buffer=B + 2 * n - 2), abi.ZERO_EALIAS), (dict(m=A + 4), abi.ZERO_EALIAS),
+                      (dict(coef=0), abi.ZERO_EINVAL)):
+        with pytest.raises(abi.ZeroError) as e:
+            h.begin(**dict(args, **bad))
+        assert e.value.code == code, bad
+    with pytest.raises(abi.ZeroError) as e:              # nothing has begun
+        h.end(B, stream=0)
+    assert e.value.code == abi.ZERO_EINVAL
+    h.close()
+    with pytest.raises(abi.ZeroError):
+        abi.Offload(0)
+
+
 def test_grad_norm_rejects():
     base = dict(grad=None, n=100, dtype=1, inv_loss_scale=1.0, workspace=W, n_sets=1, extra_sumsq=None,
                 n_extra=0, max_norm=1.0, flag=F, norm_out=F + 8, coef_out=F + 16, stream=0,

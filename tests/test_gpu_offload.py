@@ -113,3 +113,88 @@ def test_offload_rejects(abi):
     assert e.value.code == abi.ZERO_EINVAL and "clip multiplier" in str(e.value)
     got = _offload(abi, g, p, m, v, "bf16", "bf16", 1, 1.0, 0, 576)     # and the next call works
     assert not np.array_equal(got[0], p)
+
+
+# ---------------------------------------------------------------------------
+# the one-step-delayed update (zero_offload_begin / zero_offload_end)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gdt, pdt", [("bf16", "bf16"), ("f16", "f16")])
+@pytest.mark.parametrize("n, threads", [(100_003, 4), (64, 16), (1, 1)])
+def test_delayed_updates_equal_the_oracle_sequence(abi, gdt, pdt, n, threads):
+    # Three steps through begin/end; each update is the oracle's from the
+    # previous state, bit for bit, and the device parameters of step t reach
+    # the device only when step t ends (one step late).
+    _note(f"delayed offload {gdt}->{pdt} n={n} threads={threads}")
+    rng = np.random.default_rng(n + threads)
+    h = abi.Offload(threads)
+    dbuf = torch.empty(2 * n, dtype=torch.int16, device="cuda")
+    staging = torch.empty(64 + 8 * 4096, dtype=torch.uint8, pin_memory=True)     # several chunks at n = 100003
+    _, p, m, v = _inputs(n, gdt, 77)
+    hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
+    dparam = torch.full((n,), 5, dtype=torch.int16, device="cuda")
+    state = (p, m, v)
+    prev_bits = np.full(n, 5, np.uint16)
+    for t in range(1, 4):
+        g = rounding.narrow((rng.standard_normal(n) * 1e-3 / HP.inv_loss_scale).astype(np.float32), gdt)
+        coef = np.float32(0.5 + 0.1 * t)
+        dg = torch.from_numpy(g.view(np.int16).copy()).cuda()
+        dcoef = torch.tensor([coef], dtype=torch.float32, device="cuda")
+        dflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        h.begin(hm, hmm, hv, dg, gdt, n, _abi_hp(abi, HP, t), dcoef, dflag, pdt, dbuf, staging)
+        dg.fill_(0)                               # the device may reuse the gradient buffer at once
+        assert np.array_equal(dparam.cpu().numpy().view(np.uint16), prev_bits)   # still the last step's
+        assert h.end(dparam) is True
+        ref = step.adam_update(*state, g, gdt, HP, t, coef, pdt)
+        got = (hm.numpy(), hmm.numpy(), hv.numpy(), dparam.cpu().numpy().view(np.uint16))
+        adam_parity(got, ref, pdt, f"delayed step {t}")
+        state, prev_bits = ref[:3], ref[3]
+    h.close()
+
+
+def test_delayed_update_skips_on_the_flag_and_guards_its_order(abi):
+    n = 5000
+    h = abi.Offload(2)
+    dbuf = torch.empty(2 * n, dtype=torch.int16, device="cuda")
+    staging = torch.empty(64 + 8 * 1024, dtype=torch.uint8, pin_memory=True)
+    g, p, m, v = _inputs(n, "bf16", 3)
+    hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
+    dg = torch.from_numpy(g.view(np.int16).copy()).cuda()
+    dparam = torch.full((n,), 9, dtype=torch.int16, device="cuda")
+    dcoef = torch.ones(1, dtype=torch.float32, device="cuda")
+    flag = torch.tensor([abi.ZERO_FLAG_NONFINITE_GRAD], dtype=torch.int32, device="cuda")
+    with pytest.raises(abi.ZeroError) as e:                 # nothing has begun
+        h.end(dparam)
+    assert e.value.code == abi.ZERO_EINVAL
+    h.begin(hm, hmm, hv, dg, "bf16", n, _abi_hp(abi, HP, 1), dcoef, flag, "bf16", dbuf, staging)
+    with pytest.raises(abi.ZeroError) as e:                 # one update in flight at a time
+        h.begin(hm, hmm, hv, dg, "bf16", n, _abi_hp(abi, HP, 1), dcoef, flag, "bf16", dbuf, staging)
+    assert e.value.code == abi.ZERO_EINVAL
+    assert h.end(dparam) is False                           # skipped: nothing moved
+    assert np.array_equal(hm.numpy(), p) and np.all(dparam.cpu().numpy() == 9)
+    h.close()
+
+
+def test_delayed_workload_lags_one_step_and_ends_equal(abi):
+    # The shrunk 8-rank ZeRO-2 share with ZeRO-Offload, delayed and not: while
+    # step t+1's reduce runs, the delayed run's device parameters are those of
+    # step t-1; after its flush both runs hold the same state, bit for bit.
+    import dataclasses
+    from zero_sharded_mixed_flat_amd import runner, workloads
+    shrink = dict(psi=8 * 200_001 + 5, units=(8 * 200_001 + 5,), max_norm=0.01)
+    plain = runner.RankStep(dataclasses.replace(workloads.get("llama3_8b_nd8_z2_offload"), **shrink), seed=8)
+    delayed = runner.RankStep(dataclasses.replace(workloads.get("llama3_8b_nd8_z2_offload_delayed"), **shrink), seed=8)
+    history = [synth.bits(plain.param_out(0)).copy()]
+    for t in range(1, 4):
+        plain.step()
+        delayed.step()
+        torch.cuda.synchronize()
+        history.append(synth.bits(plain.param_out(0)).copy())
+        # the delayed run has ended step t-1's update only
+        assert np.array_equal(synth.bits(delayed.param_out(0)), history[t - 1]), t
+    assert delayed.flush() is True
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.bits(delayed.param_out(0)), history[3])
+    for a, b in ((plain.master, delayed.master), (plain.m, delayed.m), (plain.v, delayed.v)):
+        assert np.array_equal(a.numpy().view(np.uint32), b.numpy().view(np.uint32))
+    assert plain.counters()[:3] == delayed.counters()[:3] == (4, 3, 0)

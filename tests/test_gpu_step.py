@@ -131,6 +131,7 @@ SHRUNK = {
     # the smaller norms (about 0.016, 0.15, 0.078 and 0.10).
     "llama3_8b_nd8_z2": dict(psi=8 * 200_001 + 5, units=(8 * 200_001 + 5,), max_norm=0.01),
     "llama3_8b_nd8_z2_offload": dict(psi=8 * 200_001 + 5, units=(8 * 200_001 + 5,), max_norm=0.01),
+    "llama3_8b_nd8_z2_offload_delayed": dict(psi=8 * 200_001 + 5, units=(8 * 200_001 + 5,), max_norm=0.01),
     "paper_7p5b_nd64_z3": dict(psi=6 * 156_250, units=(156_250,) * 6, max_norm=0.1),
     "paper_7p5b_nd64_z3_qwz8": dict(psi=6 * 156_250, units=(156_250,) * 6, max_norm=0.1),
     "paper_7p5b_nd64_z3_qwz4": dict(psi=6 * 156_250, units=(156_250,) * 6, max_norm=0.1),
@@ -165,6 +166,7 @@ def test_shrunk_layouts_two_steps(runner, name):
     for t in (1, 2):
         reduced, norm, coef, p, m, v, bits = _single_rank_reference(run, w, state, t)
         run.step()
+        run.flush()              # a delayed host update ends here
         torch.cuda.synchronize()
         _note(f"  t={t}: norm gpu {run.norm.item():.9g} oracle {norm:.9g} coef {float(coef):.6g}")
         assert int(run.flag.item()) == 0

@@ -42,6 +42,7 @@ EXPORTED = (
     "zero_gather_dequant", "zero_cpu_adam_step", "zero_offload_adam_step", "zero_cpu_isa", "zero_cpu_set_isa",
     "zero_plan_reshard", "zero_ckpt_save", "zero_ckpt_load", "zero_adam_consts_fill", "zero_adam_step_consts",
     "zero_grad_norm_noalloc", "zero_reduce_owners", "zero_adam_step_owners", "zero_step_end",
+    "zero_offload_create", "zero_offload_destroy", "zero_offload_begin", "zero_offload_end",
 )
 ZERO_QBLOCK = 256
 ZERO_CPU_SCALAR = 0
@@ -135,6 +136,11 @@ _sig = {
                                 _P, _I, _I]),
     "zero_offload_adam_step": (_I, [_P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _P, _I,
                                     _P, _I64, _I, _P]),
+    "zero_offload_create": (_I, [_I, ctypes.POINTER(_P)]),
+    "zero_offload_destroy": (None, [_P]),
+    "zero_offload_begin": (_I, [_P, _P, _P, _P, _P, _I, _I64, ctypes.POINTER(zero_adam_hparams), _P, _P, _I, _P,
+                                _I64, _P, _I64, _P]),
+    "zero_offload_end": (_I, [_P, _P, ctypes.POINTER(_I), _P]),
     "zero_plan_reshard": (_I, [_P, _P, _I, ctypes.POINTER(zero_reshard_segment), _I, ctypes.POINTER(_I)]),
     "zero_ckpt_save": (_I, [ctypes.c_char_p, _P, _I, _I64, _P, _P, _P, _I, _P, _I64, _P]),
     "zero_ckpt_load": (_I, [ctypes.POINTER(ctypes.c_char_p), _I, _P, _I, _P, _P, _P, _I, ctypes.POINTER(_I64), _P,
@@ -577,6 +583,58 @@ def zero_offload_adam_step(master, m, v, grad, grad_dtype, n, hp, coef, flag, pa
                                       ctypes.byref(hp), _ptr(coef), _ptr(flag), _ptr(param_out),
                                       _dtype(param_dtype), _ptr(staging), int(sb), int(n_threads),
                                       _stream(stream)))
+
+
+class Offload:
+    """A zero_offload handle: the one-step-delayed host AdamW (begin / end)."""
+
+    def __init__(self, n_threads):
+        self.handle = _P()
+        handle = _P()
+        _check(lib.zero_offload_create(int(n_threads), ctypes.byref(handle)))
+        self.handle = handle
+        self._n = None                 # n of the update in flight
+        self._keep = None              # buffers the update in flight uses
+
+    def close(self):
+        if self.handle and lib is not None:
+            lib.zero_offload_destroy(self.handle)
+            self.handle = _P()
+
+    def __del__(self):
+        self.close()
+
+    def begin(self, master, m, v, grad, grad_dtype, n, hp, coef, flag, param_dtype, device_buffer, staging,
+              stream=None, device_bytes=None, staging_bytes=None):
+        for t, b, what in ((master, 4 * n, "master"), (m, 4 * n, "m"), (v, 4 * n, "v")):
+            _need_host(t, b, what)
+        _need_host(staging, ZERO_OFFLOAD_MIN_STAGING, "staging")
+        for t, b, what in ((grad, 2 * n, "grad"), (coef, 4, "coef"), (flag, 4, "flag"),
+                           (device_buffer, 4 * n, "device_buffer")):
+            _need(t, b, what)
+        db = _nbytes(device_buffer) if device_bytes is None else device_bytes
+        sb = _nbytes(staging) if staging_bytes is None else staging_bytes
+        _check(lib.zero_offload_begin(self.handle, _ptr(master), _ptr(m), _ptr(v), _ptr(grad), _dtype(grad_dtype),
+                                      int(n), ctypes.byref(hp), _ptr(coef), _ptr(flag), _dtype(param_dtype),
+                                      _ptr(device_buffer), int(db), _ptr(staging), int(sb), _stream(stream)))
+        self._n = int(n)
+        self._keep = (master, m, v, device_buffer, staging)
+
+    def end(self, param_out, stream=None):
+        """Finish the update in flight; returns True if it was applied."""
+        if self._n is not None:
+            _need(param_out, 2 * self._n, "param_out")
+        applied = _I()
+        rc = lib.zero_offload_end(self.handle, _ptr(param_out), ctypes.byref(applied), _stream(stream))
+        if rc != ZERO_EINVAL:              # the update has ended (applied, skipped or failed)
+            self._n = None
+            self._keep = None
+        _check(rc)
+        return bool(applied.value)
+
+    @property
+    def in_flight(self):
+        return self._n is not None
 
 
 # ---------------------------------------------------------------------------

@@ -25,8 +25,12 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <condition_variable>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <memory>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -254,27 +258,107 @@ void adam_range(int isa, const HostAdam& c, float* p, float* m, float* v, const 
 constexpr int kMaxThreads = 256;
 constexpr int64_t kMinPerThread = 1 << 15;  // smaller ranges are not worth a thread
 
-// Split [0, n) into contiguous, 64-element-aligned ranges, one per thread; the
-// calling thread takes the first.
-void adam_threads(const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt, uint16_t* out,
-                  int pdt, int64_t n, int n_threads) {
-    const int isa = g_isa.load();
+// Worker threads that live across calls.  start() hands parts 0..parts-1 of
+// a job to the workers and returns; wait() returns once every part is done.
+// One job at a time: the owner of the pool orders start and wait.
+class WorkerPool {
+  public:
+    explicit WorkerPool(int n) {
+        threads_.reserve(n);
+        for (int i = 0; i < n; ++i) threads_.emplace_back([this] { loop(); });
+    }
+    ~WorkerPool() {
+        {
+            std::lock_guard<std::mutex> lock(mu_);
+            stop_ = true;
+        }
+        work_.notify_all();
+        for (auto& t : threads_) t.join();
+    }
+    int size() const { return int(threads_.size()); }
+    void start(int parts, std::function<void(int)> fn) {
+        std::lock_guard<std::mutex> lock(mu_);
+        job_ = std::move(fn);
+        parts_ = parts;
+        next_ = 0;
+        done_ = 0;
+        ++generation_;
+        work_.notify_all();
+    }
+    void wait() {
+        std::unique_lock<std::mutex> lock(mu_);
+        finished_.wait(lock, [this] { return done_ == parts_; });
+        job_ = nullptr;
+    }
+
+  private:
+    void loop() {
+        uint64_t seen = 0;
+        std::unique_lock<std::mutex> lock(mu_);
+        for (;;) {
+            work_.wait(lock, [&] { return stop_ || (generation_ != seen && next_ < parts_); });
+            if (stop_) return;
+            seen = generation_;
+            while (next_ < parts_) {
+                const int k = next_++;
+                lock.unlock();
+                job_(k);
+                lock.lock();
+                if (++done_ == parts_) finished_.notify_all();
+            }
+        }
+    }
+    std::mutex mu_;
+    std::condition_variable work_, finished_;
+    std::vector<std::thread> threads_;
+    std::function<void(int)> job_;
+    int parts_ = 0, next_ = 0, done_ = 0;
+    uint64_t generation_ = 0;
+    bool stop_ = false;
+};
+
+// Contiguous, 64-element-aligned parts of [0, n), at most n_threads of them.
+struct Split {
+    int parts;
+    int64_t per;
+};
+
+Split split(int64_t n, int n_threads) {
     const int64_t by_size = std::max<int64_t>(1, n / kMinPerThread);
     const int t = int(std::min<int64_t>(n_threads, by_size));
-    if (t <= 1) {
-        adam_range(isa, c, p, m, v, g16, gdt, out, pdt, 0, n);
+    const int64_t per = ((n + t - 1) / t + 63) / 64 * 64;
+    return Split{int((n + per - 1) / per), per};
+}
+
+std::function<void(int)> adam_job(const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt,
+                                  uint16_t* out, int pdt, int64_t n, int64_t per) {
+    const int isa = g_isa.load();
+    return [=](int k) {
+        const int64_t lo = std::min<int64_t>(n, k * per), hi = std::min<int64_t>(n, lo + per);
+        if (lo < hi) adam_range(isa, c, p, m, v, g16, gdt, out, pdt, lo, hi);
+    };
+}
+
+// The workers of the synchronous host AdamW calls, shared by the process and
+// grown to the largest thread count asked for (calls run one at a time).
+std::mutex g_pool_mutex;
+std::unique_ptr<WorkerPool> g_pool;
+
+// The whole range on n_threads workers; returns when the update is done.
+void adam_threads(const HostAdam& c, float* p, float* m, float* v, const uint16_t* g16, int gdt, uint16_t* out,
+                  int pdt, int64_t n, int n_threads) {
+    const Split sp = split(n, n_threads);
+    if (sp.parts <= 1) {
+        adam_range(g_isa.load(), c, p, m, v, g16, gdt, out, pdt, 0, n);
         return;
     }
-    const int64_t per = ((n + t - 1) / t + 63) / 64 * 64;
-    std::vector<std::thread> pool;
-    pool.reserve(t - 1);
-    for (int k = 1; k < t; ++k) {
-        const int64_t lo = std::min<int64_t>(n, k * per), hi = std::min<int64_t>(n, lo + per);
-        if (lo >= hi) break;
-        pool.emplace_back(adam_range, isa, std::cref(c), p, m, v, g16, gdt, out, pdt, lo, hi);
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    if (!g_pool || g_pool->size() < sp.parts) {
+        g_pool.reset();
+        g_pool = std::make_unique<WorkerPool>(sp.parts);
     }
-    adam_range(isa, c, p, m, v, g16, gdt, out, pdt, 0, std::min<int64_t>(n, per));
-    for (auto& th : pool) th.join();
+    g_pool->start(sp.parts, adam_job(c, p, m, v, g16, gdt, out, pdt, n, sp.per));
+    g_pool->wait();
 }
 
 constexpr int64_t kOffloadMinStaging = ZERO_OFFLOAD_MIN_STAGING;  // head room + four slots of 64 values
@@ -345,8 +429,65 @@ int check_host_buffers(const char* fn, float* master, float* m, float* v, const 
     return ZERO_OK;
 }
 
+using HostUpdate = std::function<void(const HostAdam&, float*, float*, float*, const uint16_t*, uint16_t*, int64_t)>;
+
+// The offloaded update of [0, n) in chunks through two gradient slots and two
+// parameter slots of pinned staging, on stream s: chunk k's gradient comes to
+// the host (slot k%2), the host AdamW updates it, its parameters go back from
+// slot k%2.  The copy of chunk k+1 is queued before chunk k is updated, and a
+// slot's parameters are rewritten only after their copy to the device is
+// done.  Returns once every copy has been queued; the caller synchronises s.
+int stream_chunks(const char* fn, const HostAdam& c, float* master, float* m, float* v, const uint16_t* g_dev,
+                  int grad_dtype, uint16_t* p_dev, int param_dtype, int64_t n, uint16_t* const gslot[2],
+                  uint16_t* const pslot[2], int64_t chunk, hipEvent_t got[2], hipEvent_t sent[2], hipStream_t s,
+                  const HostUpdate& update) {
+    (void)grad_dtype;
+    (void)param_dtype;
+    auto status = [&](hipError_t e) { return e == hipSuccess ? ZERO_OK : hip_fail(e, fn); };
+    const int64_t n_chunks = (n + chunk - 1) / chunk;
+    auto enqueue_in = [&](int64_t k) {
+        const int64_t lo = k * chunk, len = std::min(chunk, n - lo);
+        hipError_t e = hipMemcpyAsync(gslot[k & 1], g_dev + lo, 2 * len, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipEventRecord(got[k & 1], s);
+        return status(e);
+    };
+    int rc = enqueue_in(0);
+    bool sent_pending[2] = {false, false};
+    for (int64_t k = 0; k < n_chunks && rc == ZERO_OK; ++k) {
+        const int64_t lo = k * chunk, len = std::min(chunk, n - lo);
+        if (k + 1 < n_chunks) rc = enqueue_in(k + 1);
+        if (rc == ZERO_OK) rc = status(hipEventSynchronize(got[k & 1]));
+        if (rc == ZERO_OK && sent_pending[k & 1]) rc = status(hipEventSynchronize(sent[k & 1]));
+        if (rc != ZERO_OK) break;
+        update(c, master + lo, m + lo, v + lo, gslot[k & 1], pslot[k & 1], len);
+        rc = status(hipMemcpyAsync(p_dev + lo, pslot[k & 1], 2 * len, hipMemcpyHostToDevice, s));
+        if (rc == ZERO_OK) rc = status(hipEventRecord(sent[k & 1], s));
+        sent_pending[k & 1] = true;
+    }
+    return rc;
+}
+
+// State of a one-step-delayed update between its begin and end calls.
+struct Pending {
+    bool active = false;
+    bool applied = false;
+    int64_t n = 0;
+    uint16_t* next_params = nullptr;   // the parameters in flight, in the caller's device buffer
+};
+
 }  // namespace
 }  // namespace zf
+
+// The host side of the delayed ZeRO-Offload update: persistent workers for the
+// host AdamW and, while an update is in flight, the thread that drives its
+// copies on a stream of its own.
+struct zero_offload {
+    std::unique_ptr<zf::WorkerPool> pool;
+    std::thread driver;
+    int driver_rc = ZERO_OK;
+    std::string driver_msg;
+    zf::Pending pending;
+};
 
 using namespace zf;
 
@@ -443,35 +584,171 @@ int zero_offload_adam_step(float* master, float* m, float* v, const void* grad_d
         rc = fail(ZERO_EINVAL, std::string(fn) + ": the clip multiplier on the device is not finite and positive");
     if (rc == ZERO_OK) c.gs = double(hp->inv_loss_scale) * double(*coef_h);
 
-    // Chunk k: gradient in (slot k%2) -> host AdamW -> parameters out (slot k%2).
-    // The copy of chunk k+1 is queued before chunk k is updated, and a slot's
-    // parameters are rewritten only after their copy to the device is done.
-    const int64_t n_chunks = (n + chunk - 1) / chunk;
-    auto enqueue_in = [&](int64_t k) {
-        const int64_t lo = k * chunk, len = std::min(chunk, n - lo);
-        hipError_t e = hipMemcpyAsync(gslot[k & 1], g_dev + lo, 2 * len, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipEventRecord(got[k & 1], s);
-        return status(e);
-    };
-    if (rc == ZERO_OK) rc = enqueue_in(0);
-    bool sent_pending[2] = {false, false};
-    for (int64_t k = 0; k < n_chunks && rc == ZERO_OK; ++k) {
-        const int64_t lo = k * chunk, len = std::min(chunk, n - lo);
-        if (k + 1 < n_chunks) rc = enqueue_in(k + 1);
-        if (rc == ZERO_OK) rc = status(hipEventSynchronize(got[k & 1]));
-        if (rc == ZERO_OK && sent_pending[k & 1]) rc = status(hipEventSynchronize(sent[k & 1]));
-        if (rc != ZERO_OK) break;
-        adam_threads(c, master + lo, m + lo, v + lo, gslot[k & 1], grad_dtype, pslot[k & 1], param_dtype, len,
-                     n_threads);
-        rc = status(hipMemcpyAsync(p_dev + lo, pslot[k & 1], 2 * len, hipMemcpyHostToDevice, s));
-        if (rc == ZERO_OK) rc = status(hipEventRecord(sent[k & 1], s));
-        sent_pending[k & 1] = true;
-    }
+    if (rc == ZERO_OK)
+        rc = stream_chunks(fn, c, master, m, v, g_dev, grad_dtype, p_dev, param_dtype, n, gslot, pslot, chunk, got,
+                           sent, s, [&](const HostAdam& cc, float* pp, float* mm, float* vv, const uint16_t* gg,
+                                        uint16_t* oo, int64_t len) {
+                               adam_threads(cc, pp, mm, vv, gg, grad_dtype, oo, param_dtype, len, n_threads);
+                           });
     // The staging buffer is the caller's again only once every copy has ended.
     const hipError_t e = hipStreamSynchronize(s);
     if (rc == ZERO_OK) rc = status(e);
     cleanup();
     return rc == ZERO_OK ? ok() : rc;
+}
+
+int zero_offload_create(int n_threads, zero_offload** out) {
+    const char* fn = "zero_offload_create";
+    if (out == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": out is NULL");
+    *out = nullptr;
+    if (n_threads < 1 || n_threads > kMaxThreads)
+        return fail(ZERO_EINVAL, std::string(fn) + ": n_threads must be in [1, 256]");
+    std::unique_ptr<zero_offload> h(new (std::nothrow) zero_offload());
+    if (!h) return fail(ZERO_ENOMEM, std::string(fn) + ": out of host memory");
+    h->pool = std::make_unique<WorkerPool>(n_threads);
+    *out = h.release();
+    return ok();
+}
+
+void zero_offload_destroy(zero_offload* h) {
+    if (h == nullptr) return;
+    if (h->driver.joinable()) h->driver.join();
+    delete h;
+}
+
+int zero_offload_begin(zero_offload* h, float* master, float* m, float* v, const void* grad_dev, int grad_dtype,
+                       int64_t n, const zero_adam_hparams* hp, const float* coef_dev, const int32_t* flag_dev,
+                       int param_dtype, void* device_buffer, int64_t device_bytes, void* staging,
+                       int64_t staging_bytes, void* stream) {
+    const char* fn = "zero_offload_begin";
+    if (h == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": handle is NULL");
+    if (h->pending.active) return fail(ZERO_EINVAL, std::string(fn) + ": the previous update has not ended");
+    if (n < 0 || n > ZERO_MAX_ELEMS) return fail(ZERO_EINVAL, std::string(fn) + ": n must be in [0, 2^34]");
+    if (!valid_dtype_h(grad_dtype) || !valid_dtype_h(param_dtype))
+        return fail(ZERO_EINVAL, std::string(fn) + ": dtypes must be ZERO_F16 or ZERO_BF16");
+    HostAdam c;
+    if (int rc = make_consts(fn, hp, 1.0f, &c)) return rc;
+    if (coef_dev == nullptr || (addr_h(coef_dev) & 3) || flag_dev == nullptr || (addr_h(flag_dev) & 3))
+        return fail(ZERO_EINVAL, std::string(fn) + ": coef_dev or flag NULL or misaligned");
+    if (staging == nullptr || (addr_h(staging) & 63) || staging_bytes < kOffloadMinStaging)
+        return fail(ZERO_EINVAL, std::string(fn) + ": staging must be 64-byte aligned and at least " +
+                                     std::to_string(kOffloadMinStaging) + " bytes");
+    if (n > 0) {
+        if (!master || !m || !v || !grad_dev) return fail(ZERO_EINVAL, std::string(fn) + ": NULL buffer");
+        if ((addr_h(master) | addr_h(m) | addr_h(v)) & 3)
+            return fail(ZERO_EINVAL, std::string(fn) + ": fp32 buffers must be 4-byte aligned");
+        if ((addr_h(grad_dev) | addr_h(device_buffer)) & 1)
+            return fail(ZERO_EINVAL, std::string(fn) + ": 16-bit buffers must be 2-byte aligned");
+        if (device_buffer == nullptr || device_bytes < 4 * n)
+            return fail(ZERO_EINVAL, std::string(fn) + ": device_buffer NULL or smaller than 4 * n bytes");
+        const void* outs[3] = {master, m, v};
+        for (int i = 0; i < 3; ++i) {
+            for (int j = i + 1; j < 3; ++j)
+                if (overlaps_h(outs[i], 4 * n, outs[j], 4 * n))
+                    return fail(ZERO_EALIAS, std::string(fn) + ": master, m and v must not overlap");
+            if (overlaps_h(outs[i], 4 * n, staging, staging_bytes))
+                return fail(ZERO_EALIAS, std::string(fn) + ": staging overlaps the host state");
+        }
+        if (overlaps_h(device_buffer, 4 * n, grad_dev, 2 * n))
+            return fail(ZERO_EALIAS, std::string(fn) + ": device_buffer overlaps the gradient");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* st = static_cast<char*>(staging);
+    float* coef_h = reinterpret_cast<float*>(st);
+    int32_t* flag_h = reinterpret_cast<int32_t*>(st + 4);
+    hipError_t e = hipMemcpyAsync(coef_h, coef_dev, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(flag_h, flag_dev, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (*flag_h != 0 || n == 0) {            // a skipped step moves nothing
+        h->pending = Pending{true, false, n, nullptr};
+        return ok();
+    }
+    if (!(std::isfinite(*coef_h) && *coef_h > 0.0f))
+        return fail(ZERO_EINVAL, std::string(fn) + ": the clip multiplier on the device is not finite and positive");
+    c.gs = double(hp->inv_loss_scale) * double(*coef_h);
+
+    // The gradient is copied aside on the device (stream order), so the caller's
+    // next step may overwrite it at once; the update's parameters collect in the
+    // second half of device_buffer until zero_offload_end.
+    uint16_t* snapshot = static_cast<uint16_t*>(device_buffer);
+    uint16_t* next_params = snapshot + n;
+    hipEvent_t ready = nullptr;
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ready, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipMemcpyAsync(snapshot, grad_dev, size_t(2 * n), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipEventRecord(ready, s);
+    if (e != hipSuccess) {
+        if (ready) (void)hipEventDestroy(ready);
+        return hip_fail(e, fn);
+    }
+    const int64_t chunk = std::min<int64_t>(n, (staging_bytes - 64) / 8 / 64 * 64);
+    h->pending = Pending{true, true, n, next_params};
+    h->driver_rc = ZERO_OK;
+    h->driver_msg.clear();
+    WorkerPool* pool = h->pool.get();
+    h->driver = std::thread([h, pool, c, master, m, v, snapshot, next_params, grad_dtype, param_dtype, n, st, chunk,
+                             ready, dev]() {
+        const char* dfn = "zero_offload_begin (update in flight)";
+        hipStream_t s2 = nullptr;
+        hipEvent_t got[2] = {nullptr, nullptr}, sent[2] = {nullptr, nullptr};
+        hipError_t e2 = hipSetDevice(dev);
+        if (e2 == hipSuccess) e2 = hipStreamCreateWithFlags(&s2, hipStreamNonBlocking);
+        if (e2 == hipSuccess) e2 = hipStreamWaitEvent(s2, ready, 0);
+        for (int k = 0; k < 2 && e2 == hipSuccess; ++k) {
+            e2 = hipEventCreateWithFlags(&got[k], hipEventDisableTiming);
+            if (e2 == hipSuccess) e2 = hipEventCreateWithFlags(&sent[k], hipEventDisableTiming);
+        }
+        int rc = e2 == hipSuccess ? ZERO_OK : hip_fail(e2, dfn);
+        if (rc == ZERO_OK) {
+            uint16_t* gslot[2] = {reinterpret_cast<uint16_t*>(st + 64), reinterpret_cast<uint16_t*>(st + 64) + chunk};
+            uint16_t* pslot[2] = {gslot[1] + chunk, gslot[1] + 2 * chunk};
+            rc = stream_chunks(dfn, c, master, m, v, snapshot, grad_dtype, next_params, param_dtype, n, gslot, pslot,
+                               chunk, got, sent, s2,
+                               [&](const HostAdam& cc, float* pp, float* mm, float* vv, const uint16_t* gg,
+                                   uint16_t* oo, int64_t len) {
+                                   const Split sp = split(len, pool->size());
+                                   pool->start(sp.parts, adam_job(cc, pp, mm, vv, gg, grad_dtype, oo, param_dtype,
+                                                                  len, sp.per));
+                                   pool->wait();
+                               });
+        }
+        if (s2 != nullptr) {
+            const hipError_t e3 = hipStreamSynchronize(s2);   // every copy of the update has ended
+            if (rc == ZERO_OK && e3 != hipSuccess) rc = hip_fail(e3, dfn);
+            (void)hipStreamDestroy(s2);
+        }
+        for (int k = 0; k < 2; ++k) {
+            if (got[k]) (void)hipEventDestroy(got[k]);
+            if (sent[k]) (void)hipEventDestroy(sent[k]);
+        }
+        (void)hipEventDestroy(ready);
+        h->driver_rc = rc;
+        if (rc != ZERO_OK) h->driver_msg = zero_last_error();
+    });
+    return ok();
+}
+
+int zero_offload_end(zero_offload* h, void* param_dev, int* applied, void* stream) {
+    const char* fn = "zero_offload_end";
+    if (h == nullptr) return fail(ZERO_EINVAL, std::string(fn) + ": handle is NULL");
+    if (!h->pending.active) return fail(ZERO_EINVAL, std::string(fn) + ": no update has begun");
+    const Pending pd = h->pending;
+    if (pd.applied && (param_dev == nullptr || (addr_h(param_dev) & 1)))
+        return fail(ZERO_EINVAL, std::string(fn) + ": param_dev NULL or misaligned");
+    if (h->driver.joinable()) h->driver.join();
+    h->pending = Pending{};
+    if (applied != nullptr) *applied = pd.applied ? 1 : 0;
+    if (h->driver_rc != ZERO_OK) {
+        const int rc = h->driver_rc;
+        h->driver_rc = ZERO_OK;
+        return fail(rc, h->driver_msg);
+    }
+    if (!pd.applied) return ok();
+    const hipError_t e = hipMemcpyAsync(param_dev, pd.next_params, size_t(2 * pd.n), hipMemcpyDeviceToDevice,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, fn);
 }
 
 }  // extern "C"

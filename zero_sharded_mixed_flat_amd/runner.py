@@ -185,6 +185,14 @@ class RankStep:
             chunk = min(OFFLOAD_CHUNK, max(64, n))
             self.staging = self._keep("staging", "staging_host",
                                       torch.empty(64 + 8 * chunk, dtype=torch.uint8, pin_memory=True))
+        # ZeRO-Offload's one-step-delayed update: persistent host workers and
+        # pinned buffers for the gradient and parameters in flight (the library's).
+        self.offload_h = None
+        if w.offload_delay:
+            self.offload_h = abi.Offload(self.host_threads)
+            # the gradient copied aside and the parameters in flight, on the device
+            self.offload_buffer = self._keep("offload_in_flight", "work",
+                                             torch.empty(2 * n, dtype=torch.int16, device=dev))
 
         n_sets = 1 if w.pre_reduced else len(self.owners)
         self.ws = self._keep("workspace", "work",
@@ -335,6 +343,7 @@ class RankStep:
         w = self.w
         k = len(self.owners)
         if w.offload:
+            self.flush(stream)
             hp = self.hparams()
             for i in range(k):
                 abi.zero_offload_adam_step(self.master[i], self.m[i], self.v[i], self.grad_of(i), w.grad_dtype,
@@ -379,11 +388,30 @@ class RankStep:
         for u in range(self.n_units):
             self.gather_unit(u, stream)
 
+    def delayed_adam(self, stream=None):
+        """ZeRO-Offload's one-step-delayed update: the previous step's host AdamW
+        ends (its 16-bit parameters reach the device), then this step's begins
+        and runs on the host while the GPU goes on with the next step."""
+        w = self.w
+        self.flush(stream)
+        self.offload_h.begin(self.master[0], self.m[0], self.v[0], self.grad_of(0), w.grad_dtype, self.n,
+                             self.hparams(), self.coef, self.flag, w.param_dtype, self.offload_buffer, self.staging,
+                             stream)
+
+    def flush(self, stream=None):
+        """Finish a delayed host update still in flight; True if one was applied."""
+        if self.offload_h is not None and self.offload_h.in_flight:
+            return self.offload_h.end(self.param_out(0), stream)
+        return False
+
     def _enqueue(self, stream=None):
         if not self.w.pre_reduced:
             self.reduce_all(stream)
         self.norm_all(stream)
-        self.adam_all(stream)
+        if self.offload_h is not None:
+            self.delayed_adam(stream)
+        else:
+            self.adam_all(stream)
         if self.codes is not None:
             self.quantize_all(stream)
         if self.shards is not None:
@@ -517,6 +545,8 @@ def allocation_plan(w, plan):
                 ("scales", "gather_codes", 4 * w.nd * abi.zero_quant_scale_count(n))]
     if w.offload:
         out.append(("staging", "staging_host", 64 + 8 * min(OFFLOAD_CHUNK, max(64, n))))
+    if w.offload_delay:
+        out.append(("offload_in_flight", "work", 4 * n))
     n_sets = 1 if w.pre_reduced else k
     out += [("workspace", "work", abi.zero_workspace_bytes(n, n_sets)), ("flag", "work", 4), ("norm", "work", 8),
             ("coef", "work", 4), ("step_state", "work", ctypes.sizeof(abi.zero_step_state)),

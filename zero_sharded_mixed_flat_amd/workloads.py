@@ -20,6 +20,9 @@ Shapes follow the pages' examples:
   ZeRO-Offload (Lecture 18 notes §4.4): master, m and v live in host memory
   and the host AdamW updates them; the reduced gradient goes to the host and
   the 16-bit parameters come back.
+* ``llama3_8b_nd8_z2_offload_delayed``: the same with ZeRO-Offload's
+  one-step-delayed update (Lecture 18 notes §4.4): the host AdamW of step t
+  runs while the GPU reduces step t+1's gradient and takes its norm.
 * ``paper_7p5b_nd64_z3_qwz8`` / ``_qwz4``: the ZeRO-3 workload with the
   ZeRO++ quantised-weight gather (Lecture 18 notes §4.5): the rank quantises
   its updated 16-bit shard to INT8 / INT4 codes with one scale per 256
@@ -63,6 +66,8 @@ class Workload:
     gather_shard_std: float = 0.0 # other ranks' 16-bit parameter shards ~ N(0, this)
     gather_bits: int = 16         # 16: plain gather; 8 or 4: block-quantised codes
     offload: bool = False         # fp32 state in host memory, AdamW on the CPU (ZeRO-Offload)
+    offload_delay: bool = False   # ... with the one-step-delayed update (the host AdamW of step t
+                                  # overlaps the GPU's reduce and norm of step t+1)
     steps: int = 1
     align: int = 8
     tensors: tuple = field(default=None, repr=False)   # ragged tensor sizes, if any
@@ -108,6 +113,12 @@ WORKLOADS = {
             master_std=0.02, m_std=1e-5, v_std=1e-8,
             lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
             rank=7, offload=True),
+        Workload(
+            name="llama3_8b_nd8_z2_offload_delayed", psi=8_030_000_000, nd=8, stage=2, units=(8_030_000_000,),
+            grad_dtype="bf16", param_dtype="bf16", grad_std=1e-4,
+            master_std=0.02, m_std=1e-5, v_std=1e-8,
+            lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+            rank=7, offload=True, offload_delay=True),
         Workload(
             name="paper_7p5b_nd64_z3", psi=7_500_000_000, nd=64, stage=3,
             units=(156_250_000,) * 48,
