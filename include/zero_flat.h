@@ -579,9 +579,10 @@ int zero_ckpt_load(const char* const* paths, int n_paths, const zero_plan* plan,
  * zero_cpu_adam_step -- the AdamW update of zero_adam_step on HOST memory, for
  * ZeRO-Offload, which keeps the fp32 master, m and v (12 bytes per parameter)
  * in host memory and updates them with a multi-threaded, vectorised CPU Adam
- * (L18 notes §4.4).  The fp32 operation sequence of zero_adam_step, with
- * coef in place of *coef_dev, so it gives the GPU kernel's bits; the result
- * does not depend on n_threads or on the instruction set.
+ * (L18 notes §4.4).  The fp64 evaluation of zero_adam_step, operation for
+ * operation, with coef in place of *coef_dev, so it gives the GPU kernel's
+ * bits; the result does not depend on n_threads or on the instruction set.
+ * The threads persist across calls (one pool for the process).
  *
  * master, m, v: host fp32, n each, distinct, 4-byte aligned.  grad: host
  * 16-bit (`grad_dtype`), n.  param_out: host 16-bit (`param_dtype`), n.  coef:

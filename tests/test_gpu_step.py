@@ -110,6 +110,51 @@ def test_tiny_skipped_step_keeps_the_step_count(runner):
     assert np.array_equal(snaps[1][1], snaps[0][1])
 
 
+def test_gpt2_loss_scaled_overflow_skips_and_keeps_t(runner):
+    # fp16 gradients under the 2^16 loss scale, one rank's share: an inf in a
+    # peer's contribution at step 2 of 3 skips that step whole (nothing of the
+    # state changes, t stays 2); step 3 then takes t = 2.  The reduce writes in
+    # place over the rank's own contribution, so step 3 gets fresh finite
+    # gradients, as a backward pass would write them.
+    w = dataclasses.replace(workloads.get("gpt2_1p5b_nd16_z1"), **SHRUNK["gpt2_1p5b_nd16_z1"])
+    _note("GPT-2 shrunk: an overflow in the middle step")
+    run = runner.RankStep(w, seed=6)
+    hp = _hp(w)
+    own0 = run.own_grad.clone()
+    peer0 = run.contrib_block[3].clone()
+    state = (_np32(run.master[0]), _np32(run.m[0]), _np32(run.v[0]))
+    t_ref = 1
+    for k in range(3):
+        if k == 1:
+            run.contrib_block[3][777] = float("inf")
+        if k == 2:
+            run.own_grad.copy_(own0)
+            run.contrib_block[3].copy_(peer0)
+        contribs = [synth.bits(c) for c in run.contribs(0)]
+        before = (_np32(run.master[0]), _np32(run.m[0]), _np32(run.v[0]), synth.bits(run.param_out(0)))
+        run.step()
+        torch.cuda.synchronize()
+        reduced, bad = step.reduce_shard(contribs, w.grad_dtype)
+        t_dev, applied, skipped, last_flag = run.counters()
+        if bad:                                              # the oracle's reading: skipped whole, t kept
+            assert k == 1 and last_flag & 1 and (t_dev, skipped) == (t_ref, 1)
+            after = (_np32(run.master[0]), _np32(run.m[0]), _np32(run.v[0]), synth.bits(run.param_out(0)))
+            for a, b in zip(after, before):
+                assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                      b.view(np.uint32) if b.dtype == np.float32 else b)
+            continue
+        norm = step.norm_from_sumsq(step.sumsq_exact(reduced, w.grad_dtype, w.inv_loss_scale))
+        coef = step.clip_coef(norm, w.max_norm)
+        ref = step.adam_update(*state, reduced, w.grad_dtype, hp, t_ref, coef, w.param_dtype)
+        got = (_np32(run.master[0]), _np32(run.m[0]), _np32(run.v[0]), synth.bits(run.param_out(0)))
+        adam_parity(got, ref, w.param_dtype, f"step {k + 1} (t = {t_ref})",
+                    same=np.float32(run.coef.item()) == np.float32(coef))
+        state = ref[:3]
+        t_ref += 1
+        assert (t_dev, last_flag) == (t_ref, 0)
+    assert run.counters()[:3] == (3, 2, 1)
+
+
 def _single_rank_reference(run, w, state, t):
     """Oracle result for the run's one emulated owner at step t from the oracle's own state."""
     hp = _hp(w)

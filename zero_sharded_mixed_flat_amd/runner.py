@@ -49,7 +49,7 @@ TORCH16 = synth.TORCH_DTYPES
 
 
 class RankStep:
-    def __init__(self, w, seed=0, device="cuda", tile_period=None, contrib_layout="auto"):
+    def __init__(self, w, seed=0, device="cuda", tile_period=None):
         self.w = w
         self.seed = seed
         self.device = device
