@@ -78,7 +78,9 @@ def _table(abi, hp, t0, length):
     (4, 4, 262_144, 0),        # stride a multiple of 4: the vector path for every owner
     (3, 2, 100_003, 5),        # gaps between owners' slices
     (16, 5, 4_099, 1),
-    (8, 3, 1, 0)])
+    (8, 3, 1, 0),
+    (100, 2, 5_000, 4),        # more than 64 ranks: the pointer table in the workspace, owner offsets on top
+    (65, 3, 2_051, 3)])
 def test_reduce_owners_equals_per_owner_calls(abi, dtype, nd, owners, n, gap):
     _note(f"reduce owners {dtype} nd={nd} owners={owners} n={n} gap={gap}")
     rng = np.random.default_rng(nd * 101 + owners * 7 + n)
@@ -178,3 +180,26 @@ def test_step_end_advances_only_applied_steps(abi):
     abi.zero_step_end(flag, state)
     torch.cuda.synchronize()
     assert _counters(state) == (9, 2, 1, 0)
+
+
+def test_empty_owner_calls(abi):
+    # n = 0: the reduce writes one zero partial sum per owner, AdamW nothing;
+    # the norm then comes from the extra sums of squares alone; the step ends.
+    owners = 3
+    ws = torch.empty(abi.zero_workspace_bytes(0, owners), dtype=torch.uint8, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t = torch.zeros(8, dtype=torch.float16, device="cuda")
+    abi.zero_reduce_owners([t, t], 0, owners, 0, "f16", 1.0, t, 0, ws, flag)
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    coef = torch.zeros(1, dtype=torch.float32, device="cuda")
+    extra = torch.tensor([9.0, 16.0], dtype=torch.float64, device="cuda")
+    abi.zero_grad_norm(None, 0, "f16", 1.0, ws, owners, extra, 2, 1.0, flag, norm, coef)
+    p = torch.ones(8, device="cuda")
+    table = _table(abi, HP, 1, 1)
+    state = _state(abi, 1, 1)
+    abi.zero_adam_step_owners(p, p.clone(), p.clone(), 0, t, "f16", 0, 0, owners, table, 1, state, coef, flag, t, 0,
+                              "f16")
+    abi.zero_step_end(flag, state)
+    torch.cuda.synchronize()
+    assert norm.item() == 5.0 and coef.item() == np.float32(1.0 / (5.0 + 1e-6))
+    assert _counters(state) == (2, 1, 0, 0) and torch.all(p == 1).item()
