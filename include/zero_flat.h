@@ -679,9 +679,10 @@ int zero_offload_begin(zero_offload* h, float* master, float* m, float* v, const
  * parameters (param_dtype of the begin call, n values) into param_dev.
  * *applied (if not NULL) is 1 if the step was applied, 0 if it was skipped
  * (nothing moves).  Errors: ZERO_EINVAL (no update begun; param_dev NULL or
- * misaligned when the step was applied), ZERO_EHIP (including a copy or
- * launch refused while the update was in flight: master, m and v are then
- * partly updated).
+ * misaligned when the step was applied), ZERO_EALIAS (param_dev overlaps the
+ * begin call's device_buffer), ZERO_EHIP (including a copy or launch refused
+ * while the update was in flight: master, m and v are then partly updated).
+ * After ZERO_EINVAL or ZERO_EALIAS the update is still in flight: call again.
  */
 int zero_offload_end(zero_offload* h, void* param_dev, int* applied, void* stream);
 

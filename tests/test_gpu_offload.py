@@ -175,6 +175,32 @@ def test_delayed_update_skips_on_the_flag_and_guards_its_order(abi):
     h.close()
 
 
+def test_delayed_end_refuses_its_own_buffer(abi):
+    # The parameters in flight sit in the second half of the begin call's
+    # device buffer; an end that would copy them onto that buffer is refused
+    # and leaves the update in flight, and the next end applies it.
+    n = 3000
+    h = abi.Offload(2)
+    dbuf = torch.empty(2 * n, dtype=torch.int16, device="cuda")
+    staging = torch.empty(64 + 8 * 1024, dtype=torch.uint8, pin_memory=True)
+    g, p, m, v = _inputs(n, "bf16", 5)
+    hm, hmm, hv = (torch.from_numpy(a.copy()) for a in (p, m, v))
+    dg = torch.from_numpy(g.view(np.int16).copy()).cuda()
+    dcoef = torch.ones(1, dtype=torch.float32, device="cuda")
+    dflag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h.begin(hm, hmm, hv, dg, "bf16", n, _abi_hp(abi, HP, 1), dcoef, dflag, "bf16", dbuf, staging)
+    for bad in (dbuf[n:], dbuf[:n], dbuf[n // 2:n // 2 + n]):
+        with pytest.raises(abi.ZeroError) as e:
+            h.end(bad)
+        assert e.value.code == abi.ZERO_EALIAS and h.in_flight
+    dparam = torch.zeros(n, dtype=torch.int16, device="cuda")
+    assert h.end(dparam) is True and not h.in_flight
+    ref = step.adam_update(p, m, v, g, "bf16", HP, 1, np.float32(1.0), "bf16")
+    adam_parity((hm.numpy(), hmm.numpy(), hv.numpy(), dparam.cpu().numpy().view(np.uint16)), ref, "bf16",
+                "delayed step after a refused end")
+    h.close()
+
+
 def test_delayed_workload_lags_one_step_and_ends_equal(abi):
     # The shrunk 8-rank ZeRO-2 share with ZeRO-Offload, delayed and not: while
     # step t+1's reduce runs, the delayed run's device parameters are those of

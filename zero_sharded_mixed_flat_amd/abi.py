@@ -626,7 +626,7 @@ class Offload:
             _need(param_out, 2 * self._n, "param_out")
         applied = _I()
         rc = lib.zero_offload_end(self.handle, _ptr(param_out), ctypes.byref(applied), _stream(stream))
-        if rc != ZERO_EINVAL:              # the update has ended (applied, skipped or failed)
+        if rc not in (ZERO_EINVAL, ZERO_EALIAS):    # the update has ended (applied, skipped or failed)
             self._n = None
             self._keep = None
         _check(rc)

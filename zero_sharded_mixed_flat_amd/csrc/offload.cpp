@@ -737,6 +737,8 @@ int zero_offload_end(zero_offload* h, void* param_dev, int* applied, void* strea
     const Pending pd = h->pending;
     if (pd.applied && (param_dev == nullptr || (addr_h(param_dev) & 1)))
         return fail(ZERO_EINVAL, std::string(fn) + ": param_dev NULL or misaligned");
+    if (pd.applied && overlaps_h(param_dev, 2 * pd.n, pd.next_params - pd.n, 4 * pd.n))
+        return fail(ZERO_EALIAS, std::string(fn) + ": param_dev overlaps the update's device buffer");
     if (h->driver.joinable()) h->driver.join();
     h->pending = Pending{};
     if (applied != nullptr) *applied = pd.applied ? 1 : 0;

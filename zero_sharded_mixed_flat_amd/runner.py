@@ -22,6 +22,13 @@ With ZeRO-Offload the fp32 state is in host memory and the AdamW step is
     gradient to the host, host AdamW, 16-bit
     parameters back, chunk by chunk               zero_offload_adam_step
 
+or, with the one-step-delayed update, the same chunked update started on a
+thread of the library's while the GPU goes on with the next step, its
+parameters applied when that step reaches its update
+
+    the previous update's parameters in place     zero_offload_end
+    gradient copied aside, host update started    zero_offload_begin
+
 All calls go to one stream with no host synchronisation inside a step
 (except the offloaded update, which waits for its copies): the clip
 multiplier, the skip flag and the step count stay in device memory.  AdamW
@@ -185,12 +192,12 @@ class RankStep:
             chunk = min(OFFLOAD_CHUNK, max(64, n))
             self.staging = self._keep("staging", "staging_host",
                                       torch.empty(64 + 8 * chunk, dtype=torch.uint8, pin_memory=True))
-        # ZeRO-Offload's one-step-delayed update: persistent host workers and
-        # pinned buffers for the gradient and parameters in flight (the library's).
+        # ZeRO-Offload's one-step-delayed update: the library's persistent host
+        # workers, and a device buffer for the gradient copied aside (first
+        # half) and the parameters in flight (second half).
         self.offload_h = None
         if w.offload_delay:
             self.offload_h = abi.Offload(self.host_threads)
-            # the gradient copied aside and the parameters in flight, on the device
             self.offload_buffer = self._keep("offload_in_flight", "work",
                                              torch.empty(2 * n, dtype=torch.int16, device=dev))
 
@@ -266,8 +273,6 @@ class RankStep:
 
     def grad_of(self, i):
         return self.grad if self.w.pre_reduced else self.reduced[i]
-
-    # -- the step ------------------------------------------------------------
 
     # -- the step count, on the device ------------------------------------------
 
