@@ -43,10 +43,11 @@ def build(verbose=True):
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+    # The partitioner is plain host C++.
     plan_o = os.path.join(objdir, "plan.o")
-    _run([hipcc, *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
+    _run([_cxx(), *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
     objs = [plan_o]
-    # Host AdamW (host code only, built by the host compiler): IEEE fp32 with no
+    # Host AdamW (host code only, built by the host compiler): IEEE fp64 with no
     # contraction, so every instruction set gives the same bits.
     host_flags = [f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__"]
     offload_o = os.path.join(objdir, "offload.o")
