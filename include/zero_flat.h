@@ -569,8 +569,8 @@ int zero_ckpt_load(const char* const* paths, int n_paths, const zero_plan* plan,
 
 /* Instruction sets of the host AdamW (zero_cpu_isa / zero_cpu_set_isa). */
 #define ZERO_CPU_SCALAR 0
-#define ZERO_CPU_AVX2 1   /* AVX2 + F16C, 8 values per instruction */
-#define ZERO_CPU_AVX512 2 /* AVX-512 F/BW/VL + F16C, 16 values per instruction */
+#define ZERO_CPU_AVX2 1   /* AVX2 + F16C, 4 fp64 lanes per instruction */
+#define ZERO_CPU_AVX512 2 /* AVX-512 F/BW/VL + F16C, 8 fp64 lanes per instruction */
 
 /* Minimum size of the pinned staging buffer of zero_offload_adam_step. */
 #define ZERO_OFFLOAD_MIN_STAGING 576
