@@ -43,6 +43,8 @@
  * - Alignment: 16-bit pointers 2-byte aligned, fp32 pointers 4-byte aligned.
  *   Any offset works; 16-byte-aligned buffers take the vector path.
  * - Inputs may not overlap outputs (ZERO_EALIAS).
+ * - Host arrays passed in (sizes, device pointers per rank) are read before
+ *   the call returns; the caller may reuse or free them at once.
  * - A non-finite gradient is not an error: it is reported through the
  *   caller's int32 device flag and the Adam kernel then skips the step.
  */

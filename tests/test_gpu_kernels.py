@@ -411,3 +411,62 @@ def test_gather(abi, units, nd, align):
     torch.cuda.synchronize()
     step.gather(ref_plan, shards, expect)
     assert np.array_equal(_bits(full), expect)
+
+
+@pytest.mark.parametrize("quantised", [False, True])
+def test_pointer_tables_may_be_reused_at_once(abi, quantised):
+    # With more than 64 owners the shard pointers reach the kernel through a
+    # table copied into the workspace.  The call reads the caller's arrays
+    # before it returns: a caller that points its (pinned) arrays at other
+    # valid shards at once, while the stream is still busy, still gets the
+    # gather of the shards it passed.
+    import ctypes
+    _note(f"pointer tables reused at once, quantised={quantised}")
+    units, nd, align = [2560, 768], 100, 256
+    plan = abi.Plan(units, nd, 3, align)
+    ref_plan = partition.make_plan(units, nd, 3, align)
+    n = ref_plan.shard_numel
+    rng = np.random.default_rng(7)
+    sets = [[rounding.narrow((rng.standard_normal(n) * 0.02).astype(np.float32), "bf16") for _ in range(nd)]
+            for _ in range(2)]
+    dev = [[_dev16(x, "bf16") for x in shards] for shards in sets]
+    if quantised:
+        cb, nb = abi.zero_quant_code_bytes(n, 8), abi.zero_quant_scale_count(n)
+        codes = [[torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(nd)] for _ in range(2)]
+        scales = [[torch.empty(nb, dtype=torch.float32, device="cuda") for _ in range(nd)] for _ in range(2)]
+        for k in range(2):
+            for r in range(nd):
+                abi.zero_quantize_blocks(dev[k][r], "bf16", n, 8, codes[k][r], scales[k][r])
+        arrays = [[[t.data_ptr() for t in codes[k]], [t.data_ptr() for t in scales[k]]] for k in range(2)]
+    else:
+        arrays = [[[t.data_ptr() for t in dev[k]]] for k in range(2)]
+    tables = [torch.tensor(a, dtype=torch.int64).pin_memory() for a in arrays[0]]   # the caller's arrays, pinned
+    full = torch.zeros(ref_plan.full_numel, dtype=torch.bfloat16, device="cuda")
+    ws = _ws(abi, 0, 0)
+    torch.cuda.synchronize()
+    busy = torch.zeros(1 << 28, dtype=torch.uint8, device="cuda")
+    for _ in range(8):                        # queued work: the stream is busy when the call returns
+        busy.add_(1)
+    stream = torch.cuda.current_stream().cuda_stream
+    as_ptrs = [ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_void_p)) for t in tables]
+    if quantised:
+        rc = abi.lib.zero_gather_dequant(plan.handle, as_ptrs[0], as_ptrs[1], 0, 2, 8, abi.ZERO_BF16,
+                                         full.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+    else:
+        rc = abi.lib.zero_gather_params(plan.handle, as_ptrs[0], 0, 2, abi.ZERO_BF16, full.data_ptr(),
+                                        ws.data_ptr(), ws.numel(), stream)
+    for t, a in zip(tables, arrays[1]):
+        t.copy_(torch.tensor(a, dtype=torch.int64))       # at once: now the other, equally valid, shards
+    torch.cuda.synchronize()
+    assert rc == abi.ZERO_OK, abi.zero_last_error()
+    assert busy[0].item() == 8
+    got = _bits(full)
+    if quantised:
+        from oracle import quant
+        coded = [quant.quantize(x, "bf16", 8) for x in sets[0]]
+        shards = [quant.dequantize(c, sc, "bf16") for c, sc in coded]
+    else:
+        shards = sets[0]
+    expect = np.zeros(ref_plan.full_numel, np.uint16)
+    step.gather(ref_plan, shards, expect)
+    assert np.array_equal(got, expect)

@@ -1055,7 +1055,11 @@ int zero_gather_params(const zero_plan* plan, const void* const* shards, int uni
     if (device_table) {
         if (int rc = refuse_capture(s, fn)) return rc;
         dtab = static_cast<const uint16_t* const*>(workspace);
-        const hipError_t e = hipMemcpyAsync(workspace, shards, sizeof(void*) * owners, hipMemcpyHostToDevice, s);
+        // Copied from the library's own pageable copy of the pointers, which the
+        // runtime stages before returning: the caller may reuse `shards` at once,
+        // whatever memory it is in.
+        const std::vector<const void*> ptrs(shards, shards + owners);
+        const hipError_t e = hipMemcpyAsync(workspace, ptrs.data(), sizeof(void*) * owners, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_status(e, fn);
     } else {
         for (int r = 0; r < owners; ++r) tab.p[r] = static_cast<const uint16_t*>(shards[r]);

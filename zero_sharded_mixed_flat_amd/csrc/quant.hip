@@ -493,9 +493,13 @@ int zero_gather_dequant(const zero_plan* plan, const void* const* code_shards, c
         char* w = static_cast<char*>(workspace);
         dct = reinterpret_cast<const uint8_t* const*>(w);
         dst = reinterpret_cast<const float* const*>(w + kTableBytes);
-        hipError_t e = hipMemcpyAsync(w, code_shards, sizeof(void*) * owners, hipMemcpyHostToDevice, s);
+        // Copied from the library's own pageable copies of the pointers, which the
+        // runtime stages before returning: the caller may reuse its arrays at
+        // once, whatever memory they are in.
+        const std::vector<const void*> codes(code_shards, code_shards + owners), scales(scale_shards, scale_shards + owners);
+        hipError_t e = hipMemcpyAsync(w, codes.data(), sizeof(void*) * owners, hipMemcpyHostToDevice, s);
         if (e == hipSuccess)
-            e = hipMemcpyAsync(w + kTableBytes, scale_shards, sizeof(void*) * owners, hipMemcpyHostToDevice, s);
+            e = hipMemcpyAsync(w + kTableBytes, scales.data(), sizeof(void*) * owners, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_status(e, fn);
     } else {
         for (int r = 0; r < owners; ++r) {
