@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert abi.zero_version() == 10300
+    assert abi.zero_version() == 10301
 
 
 @pytest.mark.parametrize("seed", range(60))

@@ -66,7 +66,7 @@ def test_c_program_calls_the_library(tmp_path):
     assert p.returncode == 0, p.stderr
     out = dict(line.split(" ", 1) for line in p.stdout.splitlines())
     ref = partition.make_plan([1000, 37, 2050], 4, 3, 8)
-    assert out["version"] == "10300"
+    assert out["version"] == "10301"
     assert out["shard"] == f"{ref.shard_numel} real {ref.real_numel(3)} full {ref.full_numel}"
     assert float(out["bytes"]) == accounting.model_state_bytes(7.5e9, 64, 2)
     assert out["reject"] == "1 message"

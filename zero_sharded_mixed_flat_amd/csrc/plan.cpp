@@ -92,7 +92,7 @@ extern "C" {
 
 const char* zero_last_error(void) { return zf::g_error.c_str(); }
 
-int zero_version(void) { return 10300; }
+int zero_version(void) { return 10301; }
 
 int zero_plan_create(const int64_t* unit_numels, int n_units, int nd, int stage,
                      int64_t align_elems, zero_plan** out) {
